@@ -1,0 +1,193 @@
+"""Oracle for the data half of the path: permute, prefetch, GEMM, combine, grads.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+All bf16 tensors are passed as raw uint16 bit arrays.  Floating point is done
+in float64 on exact bf16 values and rounded once at the end (bf16 outputs) or
+kept in float64 (gradients); the GPU side accumulates in fp32, which the
+tolerances in the parity tests cover.
+
+Pinned by tests/test_oracle_dataflow.py: bit-copy invariants of permute and
+prefetch, closed forms with W[e] = c_e * I and constant gates, brute-force
+triple loops on tiny shapes, and known constants for reduce_grad.
+"""
+import numpy as np
+
+from . import bf16
+from .plan import segment_of_rows
+
+
+def dispatch(x_bits, plan, cfg):
+    """Fused permute: xperm[route[i]] = x[i // K].
+
+    [K3-blog] "在线规划、零拷贝、静态 shape" / [MoonEP-fr] "Communication sans
+    copie": the plan gives each routing entry its place in the destination
+    rank's expert-grouped S*K buffer and the row is written there directly.
+    Returns the [R*S*K, H] bit array (R stacked [S*K, H] buffers).
+    """
+    K = cfg.K
+    x = np.asarray(x_bits, np.uint16)
+    out = np.zeros((cfg.R * cfg.SK, cfg.H), np.uint16)
+    src_tok = np.arange(plan.route.size) // K
+    out[plan.route] = x[src_tok]
+    return out
+
+
+def prefetch(w_home_bits, plan, cfg):
+    """prefetch_weight: slot b of rank r <- home row slot_expert[r, b].
+
+    [MoonEP-news] "核心思想": rows [E, E+B) are local prefetch slots filled by
+    buffer.prefetch_weight before expert compute.  Unused slots stay zero.
+    """
+    R, B = cfg.R, cfg.B
+    w = np.asarray(w_home_bits, np.uint16)
+    out = np.zeros((R, B) + w.shape[1:], np.uint16)
+    for r in range(R):
+        for b in range(B):
+            e = plan.slot_expert[r, b]
+            if e >= 0:
+                out[r, b] = w[e]
+    return out
+
+
+def weight_row(w_home_bits, w_pref_bits, r, j, cfg):
+    """Weight addressed by row index j of the [E+B, H, H'] view of rank r.
+
+    [MoonEP-news] "核心思想": the grouped GEMM addresses experts only by row
+    index; rows [0, E) are every rank's home experts, rows [E, E+B) this
+    rank's prefetch slots.
+    """
+    if j < cfg.E:
+        return w_home_bits[j]
+    return w_pref_bits[r, j - cfg.E]
+
+
+def grouped_gemm(xperm_bits, w_home_bits, w_pref_bits, plan, cfg, ranks=None):
+    """y[rows of segment j on rank r] = xperm[rows] @ W(r, j), bf16 output.
+
+    The product of exact bf16 values is formed in float64 and rounded to
+    bf16 once.  Returns the [R*S*K, H'] bit array; rows of ranks not listed
+    in ``ranks`` are left zero.
+    """
+    R, SK, E, B = cfg.R, cfg.SK, cfg.E, cfg.B
+    y = np.zeros((R * SK, cfg.Hp), np.uint16)
+    for r in (range(R) if ranks is None else ranks):
+        for j in range(E + B):
+            lo, hi = plan.cu_seqlens[r, j], plan.cu_seqlens[r, j + 1]
+            if hi == lo:
+                continue
+            a = bf16.bits_to_f64(xperm_bits[r * SK + lo:r * SK + hi])
+            w = bf16.bits_to_f64(weight_row(w_home_bits, w_pref_bits, r, j, cfg))
+            y[r * SK + lo:r * SK + hi] = bf16.f64_to_bits(a @ w)
+    return y
+
+
+def gemm_rows(rows, x_bits, w_home_bits, w_pref_bits, plan, cfg):
+    """Oracle y for selected destination rows only (large shapes).
+
+    Row q = r*S*K + offset holds token route^-1(q) // K and belongs to weight
+    row j = its segment; y[q] = bf16(x[token] @ W(r, j)).  Rows are grouped
+    by (r, j) so each weight is converted once.
+    """
+    SK = cfg.SK
+    rows = np.asarray(rows, np.int64)
+    inv = np.empty(plan.route.size, np.int64)
+    inv[plan.route] = np.arange(plan.route.size)
+    seg = np.empty(rows.size, np.int64)
+    for idx, q in enumerate(rows):
+        r, off = divmod(int(q), SK)
+        seg[idx] = np.searchsorted(plan.cu_seqlens[r], off, side="right") - 1
+    out = np.zeros((rows.size, cfg.Hp), np.uint16)
+    keys = (rows // SK) * (cfg.E + cfg.B) + seg
+    for key in np.unique(keys):
+        sel = np.nonzero(keys == key)[0]
+        r, j = divmod(int(key), cfg.E + cfg.B)
+        tok = inv[rows[sel]] // cfg.K
+        a = bf16.bits_to_f64(np.asarray(x_bits[tok]))
+        w = bf16.bits_to_f64(weight_row(w_home_bits, w_pref_bits, r, j, cfg))
+        out[sel] = bf16.f64_to_bits(a @ w)
+    return out
+
+
+def combine(y_bits, gates, plan, cfg):
+    """out[t] = sum over k (ascending) of g[t, k] * y[route[t*K + k]].
+
+    [K3-blog] "在线规划、零拷贝、静态 shape": each expert output is multiplied
+    by its own fp32 router weight on combine; [TSR] §6.1: combine then
+    weighted sum.  Accumulated in float64, rounded to bf16 once.
+    """
+    K = cfg.K
+    g = np.asarray(gates, np.float64).reshape(-1, K)
+    nt = g.shape[0]
+    acc = np.zeros((nt, cfg.Hp), np.float64)
+    route = plan.route.reshape(nt, K)
+    y = np.asarray(y_bits, np.uint16)
+    for k in range(K):
+        acc += g[:, k:k + 1] * bf16.bits_to_f64(y[route[:, k]])
+    return bf16.f64_to_bits(acc)
+
+
+def wgrad(xperm_bits, dy_bits, plan, cfg):
+    """Weight gradients of the grouped GEMM, fp32 layout [E+B, H, H'].
+
+    G(r, j) = xperm[rows of j]^T @ dy[rows of j] (float64).  Home rows go to
+    grad_home[j] on j's home rank -- overwritten, zero when the segment is
+    empty; prefetch rows j = E+b go to grad_pref[r, b] ([MoonEP-news] "核心
+    思想": rows [E, E+B) of the gradient are backed by a separate reduce
+    buffer).  Slots that hold no expert are left as they were (zero here).
+    Train mode only (B = E/R), so there are no overflow rows.
+    """
+    R, SK, E, B, n = cfg.R, cfg.SK, cfg.E, cfg.B, cfg.n
+    gh = np.zeros((E, cfg.H, cfg.Hp), np.float64)
+    gp = np.zeros((R, B, cfg.H, cfg.Hp), np.float64)
+    for r in range(R):
+        for j in list(range(r * n, (r + 1) * n)) + list(range(E, E + B)):
+            lo, hi = plan.cu_seqlens[r, j], plan.cu_seqlens[r, j + 1]
+            if j >= E and hi == lo:
+                continue
+            a = bf16.bits_to_f64(xperm_bits[r * SK + lo:r * SK + hi])
+            d = bf16.bits_to_f64(dy_bits[r * SK + lo:r * SK + hi])
+            g = a.T @ d
+            if j < E:
+                gh[j] = g
+            else:
+                gp[r, j - E] = g
+    return gh, gp
+
+
+def reduce_grad(grad_home, grad_pref, plan, cfg):
+    """reduce_grad: fold prefetch-slot gradients into their home rows.
+
+    [MoonEP-news] "核心思想": each home reads every rank's slots of its own
+    experts, accumulates them into the local parameter gradient and zeroes
+    the consumed slots.  Order: home value first, then ranks ascending.
+    Returns new (grad_home, grad_pref) arrays (float64).
+    """
+    gh = np.array(grad_home, np.float64, copy=True)
+    gp = np.array(grad_pref, np.float64, copy=True)
+    for e in range(cfg.E):
+        for r in range(cfg.R):
+            for b in range(cfg.B):
+                if plan.slot_expert[r, b] == e:
+                    gh[e] += gp[r, b]
+    for r in range(cfg.R):
+        for b in range(cfg.B):
+            if plan.slot_expert[r, b] >= 0:
+                gp[r, b] = 0.0
+    return gh, gp
+
+
+def reduce_terms_abs(grad_home, grad_pref, plan, cfg):
+    """sum of |terms| per element of each home row's reduction (tolerances)."""
+    s = np.abs(np.asarray(grad_home, np.float64)).copy()
+    for r in range(cfg.R):
+        for b in range(cfg.B):
+            e = plan.slot_expert[r, b]
+            if e >= 0:
+                s[e] += np.abs(grad_pref[r, b])
+    return s
+
+
+__all__ = ["dispatch", "prefetch", "weight_row", "grouped_gemm", "gemm_rows",
+           "combine", "wgrad", "reduce_grad", "reduce_terms_abs",
+           "segment_of_rows"]
