@@ -1,0 +1,224 @@
+/*
+ * moonep.h -- C ABI of the MI355X (gfx950) MoonEP hot path.
+ *
+ * The path (one MoE layer, all R expert-parallel ranks held as "virtual ranks"
+ * in one GPU's memory):
+ *
+ *   moe_plan_run         router histogram + Theorem-1 planner + route map
+ *   moe_prefetch_weight  copy redundant experts into prefetch rows [E, E+B)
+ *   moe_dispatch         fused permute into expert-grouped [S*K, H] buffers
+ *   moe_grouped_gemm     grouped GEMM over the [E+B, H, H'] weight view
+ *   moe_combine          gate-weighted unpermute back to tokens
+ *   moe_grouped_gemm_wgrad  fp32 weight gradients of the grouped GEMM
+ *   moe_reduce_grad      fold prefetch-slot gradients into home rows
+ *
+ * Sources: "Kimi K3 模型结构（8）：训练并行，MoonEP 与四类等待" (blog.javazero.top),
+ * "Moonshot AI 开源 MoonEP" (feinterview), "MoonEP : l'équilibrage parfait"
+ * (mkdocs.reaper.mx); each entry point cites the passage that defines it.
+ *
+ * Conventions for every entry point:
+ *  - every pointer argument is a DEVICE pointer unless stated otherwise, and
+ *    the caller allocates and owns it; the library allocates nothing and
+ *    keeps no state between calls;
+ *  - every call is asynchronous on `stream` and never synchronises the host;
+ *  - the return value is MOE_OK or a negative MOE_E* code, detected on the
+ *    host before anything is launched (bad configuration, null pointer, a
+ *    size beyond the documented limits) or reported by the HIP launch;
+ *  - conditions only the device can see (expert ids outside [0, E)) set bits
+ *    in plan->status instead, and every later step of that plan then leaves
+ *    its outputs untouched where the route is -1;
+ *  - bf16 tensors are raw IEEE bfloat16 bit patterns (moe_bf16); rounding to
+ *    bf16 is round-to-nearest-even; all arrays are dense row-major.
+ *
+ * Notation: R ranks, S tokens per rank, E experts (E % R == 0, n = E/R home
+ * experts per rank, rank r owns experts [r*n, (r+1)*n)), K distinct experts
+ * per token, H hidden size, Hp = H' expert intermediate size, B prefetch slots
+ * per rank.  Slot i = t*K + k is the k-th route of global token t = r*S + s.
+ */
+#ifndef MOONEP_H
+#define MOONEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16;
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1, /* bad configuration, null pointer or rank range        */
+  MOE_EHIP = -2,   /* a HIP launch or runtime call failed                   */
+  MOE_ELIMIT = -3  /* a size beyond the limits below                        */
+};
+
+enum { MOE_MODE_TRAIN = 0, MOE_MODE_INFER = 1 };
+
+/* Device-side status bits (plan->status[2]). */
+enum {
+  MOE_STATUS_BAD_ID = 1,     /* some topk id outside [0, E): plan not built */
+  MOE_STATUS_UNBALANCED = 2, /* loads do not add up to R*S*K               */
+  MOE_STATUS_CAPACITY = 4,   /* train mode needed more than B slots         */
+  MOE_STATUS_INTERNAL = 8    /* a planner invariant failed                  */
+};
+
+/* Limits checked on the host (MOE_ELIMIT beyond them). */
+#define MOE_MAX_E 2048
+#define MOE_MAX_R 1024
+#define MOE_MAX_K 64
+
+/*
+ * Layer configuration.  mode = MOE_MODE_TRAIN requires B == E/R: the planner
+ * may copy up to E/R experts from one home rank, and training keeps every
+ * expert the GEMM touches local ("Moonshot AI 开源 MoonEP", 核心思想, B policy).
+ * mode = MOE_MODE_INFER allows 0 <= B <= E/R; redundant experts beyond B are
+ * computed from their home row e of the weight view (overflow).
+ * Requirements: R >= 1, S >= 0, E % R == 0, 1 <= K <= E, H % 8 == 0,
+ * Hp % 8 == 0, R*S*K < 2^31.
+ */
+typedef struct {
+  int32_t R, S, E, K, H, Hp, B, mode;
+} moe_cfg;
+
+/*
+ * Plan: a bundle of caller-allocated device arrays (sizes from
+ * moe_plan_sizes, in this field order).  Filled by moe_plan_run and read by
+ * every later step of the same layer.
+ */
+typedef struct {
+  int32_t *counts;      /* [E]            T_e, routes per expert              */
+  int32_t *load0;       /* [R]            initial load of each rank           */
+  int32_t *route;       /* [R*S*K]        destination row r*S*K + offset of
+                                          slot i; -1 if the plan failed      */
+  int32_t *cu_seqlens;  /* [R][E+B+1]     per-rank prefix over weight rows    */
+  int32_t *slot_expert; /* [R][B]         expert held by prefetch slot, or -1 */
+  int32_t *n_redundant; /* [R]            distinct remote experts received    */
+  int32_t *src_rank;    /* [R]            the single donor rank, or -1        */
+  int32_t *moves;       /* [E+R-1][4]     (e, dst, lo, hi) in fill order      */
+  int32_t *status;      /* [4]            n_fills, n_moves, status bits, 0    */
+  void *workspace;      /* opaque scratch of moe_plan_sizes()[9] bytes        */
+} moe_plan;
+
+#define MOE_PLAN_NARRAYS 10
+
+/*
+ * Host only.  Writes the byte size of each moe_plan array, in field order
+ * (counts ... status, workspace), into sizes_out[0..9].  Returns MOE_EINVAL
+ * or MOE_ELIMIT for a configuration the library cannot run.
+ */
+int moe_plan_sizes(const moe_cfg *cfg, size_t sizes_out[MOE_PLAN_NARRAYS]);
+
+/*
+ * Histogram, planner and route map ("Kimi K3 模型结构（8）", 定理 1 and
+ * 在线规划、零拷贝、静态 shape; "MoonEP : l'équilibrage parfait", Le théorème).
+ *
+ * topk_ids [R*S][K] int32: expert ids of each token, K distinct per token.
+ * Computes T_e, each rank's home load, and runs the constructive proof of
+ * Theorem 1 deterministically: while a rank holds fewer than S*K slots, the
+ * lowest-id such rank u is filled to exactly S*K from the rank with the
+ * largest load (ties: lowest id), which gives its home experts in ascending
+ * id and, inside an expert, its earliest remaining slots in (token, k)
+ * order.  At most R-1 fills; every rank ends with S*K slots, receives from
+ * one rank only and needs at most E/R redundant experts.  Then lays out each
+ * rank's S*K buffer by weight row (ascending j in [0, E+B); ascending
+ * (token, k) inside) and writes cu_seqlens, slot_expert and route.
+ * Deterministic: the same ids give bit-identical outputs.
+ */
+int moe_plan_run(const moe_cfg *cfg, const int32_t *topk_ids,
+                 const moe_plan *plan, hipStream_t stream);
+
+/*
+ * prefetch_weight ("Moonshot AI 开源 MoonEP", 核心思想: rows [E, E+B) are local
+ * prefetch slots filled by buffer.prefetch_weight).  For every rank r and
+ * slot b with slot_expert[r][b] = e >= 0, copies w_home[e] ([H][Hp] bf16)
+ * to w_pref[r][b].  Slots holding no expert are not written.
+ * w_home [E][H][Hp], w_pref [R][B][H][Hp]; they must not overlap.
+ */
+int moe_prefetch_weight(const moe_cfg *cfg, const moe_plan *plan,
+                        const moe_bf16 *w_home, moe_bf16 *w_pref,
+                        hipStream_t stream);
+
+/*
+ * Fused permute ("Kimi K3 模型结构（8）", 在线规划、零拷贝、静态 shape: rows go
+ * straight to expert-grouped places in a fixed S*K buffer per rank).
+ * xperm[route[t*K + k]] = x[t] for every token t and k; x [R*S][H] bf16,
+ * xperm [R][S*K][H] bf16.  Bit copy.  Slots with route -1 are skipped.
+ */
+int moe_dispatch(const moe_cfg *cfg, const moe_plan *plan, const moe_bf16 *x,
+                 moe_bf16 *xperm, hipStream_t stream);
+
+/*
+ * Host only.  Bytes of scratch that moe_grouped_gemm and
+ * moe_grouped_gemm_wgrad need in their `workspace` argument.
+ */
+int moe_gemm_workspace_size(const moe_cfg *cfg, size_t *bytes_out);
+
+/*
+ * Grouped GEMM over one [E+B, H, Hp] weight view addressed by row index
+ * ("Moonshot AI 开源 MoonEP", 核心思想: VM grouped GEMM, cu_seqlens[E+B]
+ * selects the active rows; rows [0, E) are every rank's home experts, rows
+ * [E, E+B) the rank's prefetch slots).  For ranks r in [rank_begin,
+ * rank_end) and rows j with cu_seqlens[r][j] < cu_seqlens[r][j+1]:
+ *   y[r][cu[j]:cu[j+1]] = bf16( xperm[r][cu[j]:cu[j+1]] @ W(r, j) )
+ * with W(r, j) = w_home[j] for j < E and w_pref[r][j-E] otherwise; products
+ * accumulate in fp32 and round once to bf16.  xperm [R][S*K][H],
+ * y [R][S*K][Hp], w_home [E][H][Hp], w_pref [R][B][H][Hp] (may be NULL when
+ * B == 0), cu_seqlens [R][E+B+1] (as written by moe_plan_run).  Rows of y
+ * outside the listed ranks are not written.  `workspace` holds
+ * moe_gemm_workspace_size() bytes; concurrent calls need distinct ones.
+ */
+int moe_grouped_gemm(const moe_cfg *cfg, const moe_bf16 *xperm,
+                     const moe_bf16 *w_home, const moe_bf16 *w_pref,
+                     const int32_t *cu_seqlens, moe_bf16 *y,
+                     int32_t rank_begin, int32_t rank_end, void *workspace,
+                     hipStream_t stream);
+
+/*
+ * Gate-weighted combine ("Kimi K3 模型结构（8）", 在线规划、零拷贝、静态 shape:
+ * each expert output is multiplied by its own fp32 router weight).
+ *   out[t] = bf16( sum_{k ascending} gates[t][k] * y[route[t*K + k]] )
+ * accumulated in fp32.  y [R][S*K][Hp] bf16, gates [R*S][K] fp32,
+ * out [R*S][Hp] bf16.  Routes of -1 contribute nothing.
+ */
+int moe_combine(const moe_cfg *cfg, const moe_plan *plan, const moe_bf16 *y,
+                const float *gates, moe_bf16 *out, hipStream_t stream);
+
+/*
+ * Weight gradients of the grouped GEMM, fp32 ("Moonshot AI 开源 MoonEP",
+ * 核心思想: training mirrors the weight layout in fp32; rows [E, E+B) are
+ * backed by a separate reduce buffer).  Train mode only.  For every rank r:
+ *   grad_home[j]   = xperm_seg(r, j)^T @ dy_seg(r, j)  for r's home rows j
+ *                    (overwritten; zero when the segment is empty)
+ *   grad_pref[r][b] = the same for row E+b, for every slot b holding an
+ *                    expert; other slots are not written.
+ * xperm [R][S*K][H] bf16, dy [R][S*K][Hp] bf16, grad_home [E][H][Hp],
+ * grad_pref [R][B][H][Hp].  `workspace` as for moe_grouped_gemm.
+ */
+int moe_grouped_gemm_wgrad(const moe_cfg *cfg, const moe_plan *plan,
+                           const moe_bf16 *xperm, const moe_bf16 *dy,
+                           float *grad_home, float *grad_pref,
+                           void *workspace, hipStream_t stream);
+
+/*
+ * reduce_grad ("Moonshot AI 开源 MoonEP", 核心思想: each rank reads its own
+ * experts' slots from every rank, accumulates them into its parameter
+ * gradient and zeroes the consumed slots).  For every expert e:
+ *   grad_home[e] += sum over ranks r ascending of grad_pref[r][b],
+ *                   slot_expert[r][b] == e
+ * in fp32, then every slot with slot_expert >= 0 is set to zero; other slots
+ * are untouched.
+ */
+int moe_reduce_grad(const moe_cfg *cfg, const moe_plan *plan, float *grad_home,
+                    float *grad_pref, hipStream_t stream);
+
+/* Host only.  Static text for a MOE_* return code. */
+const char *moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOONEP_H */

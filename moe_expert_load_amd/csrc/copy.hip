@@ -1,0 +1,266 @@
+// HBM-bound steps: prefetch_weight, fused permute (dispatch), gate-weighted
+// combine and reduce_grad.  Every row moves as 16-byte vectors; a wave owns a
+// token (dispatch, combine) so its K routes are read once and broadcast with
+// lane shuffles.
+//
+// Sources: "Kimi K3 模型结构（8）：训练并行，MoonEP 与四类等待", heading
+// 在线规划、零拷贝、静态 shape (permute straight into expert-grouped places;
+// combine multiplies each expert output by its own fp32 router weight);
+// "Moonshot AI 开源 MoonEP", 核心思想 (prefetch_weight fills rows [E, E+B);
+// reduce_grad folds each rank's slots of an expert into its home gradient and
+// zeroes the consumed slots).
+#include "common.hpp"
+#include "host.hpp"
+
+namespace moonep {
+
+// ---------------------------------------------------------------------------
+// prefetch: grid (chunks, R*B); slot s = r*B + b copies w_home[slot_expert[s]].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prefetch(const u32x4* __restrict__ w_home,
+                                                  u32x4* __restrict__ w_pref,
+                                                  const int32_t* __restrict__ slot_expert,
+                                                  int64_t nvec) {
+  const int slot = blockIdx.y;
+  const int e = slot_expert[slot];
+  if (e < 0) return;
+  const u32x4* src = w_home + int64_t(e) * nvec;
+  u32x4* dst = w_pref + int64_t(slot) * nvec;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; v + 3 * stride < nvec; v += 4 * stride) {
+    const u32x4 a0 = src[v], a1 = src[v + stride], a2 = src[v + 2 * stride],
+                a3 = src[v + 3 * stride];
+    __builtin_nontemporal_store(a0, dst + v);
+    __builtin_nontemporal_store(a1, dst + v + stride);
+    __builtin_nontemporal_store(a2, dst + v + 2 * stride);
+    __builtin_nontemporal_store(a3, dst + v + 3 * stride);
+  }
+  for (; v < nvec; v += stride) __builtin_nontemporal_store(src[v], dst + v);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch: one wave per token; the row is read once (DU vectors per lane per
+// pass) and written to each of its K destinations.
+// ---------------------------------------------------------------------------
+template <int DU>
+__global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
+                                                  u32x4* __restrict__ xperm,
+                                                  const int32_t* __restrict__ route, int ntok,
+                                                  int K, int hv) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= ntok) return;
+  const int lane = lane_id();
+  const int myroute = lane < K ? route[int64_t(t) * K + lane] : -1;
+  const u32x4* src = x + int64_t(t) * hv;
+  for (int c0 = 0; c0 < hv; c0 += kWave * DU) {
+    u32x4 v[DU];
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < hv) v[u] = src[c];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int dst = __shfl(myroute, k, kWave);
+      if (dst < 0) continue;
+      u32x4* d = xperm + int64_t(dst) * hv;
+#pragma unroll
+      for (int u = 0; u < DU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < hv) __builtin_nontemporal_store(v[u], d + c);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: one wave per token; out = sum_k g_k * y[route_k] in fp32, k
+// ascending, rounded once to bf16.
+// ---------------------------------------------------------------------------
+template <int CU>
+__global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
+                                                 const float* __restrict__ gates,
+                                                 const int32_t* __restrict__ route,
+                                                 u32x4* __restrict__ out, int ntok, int K,
+                                                 int hv) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= ntok) return;
+  const int lane = lane_id();
+  const int myroute = lane < K ? route[int64_t(t) * K + lane] : -1;
+  const float mygate = lane < K ? gates[int64_t(t) * K + lane] : 0.f;
+  for (int c0 = 0; c0 < hv; c0 += kWave * CU) {
+    float acc[CU][8];
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int src = __shfl(myroute, k, kWave);
+      const float g = __shfl(mygate, k, kWave);
+      if (src < 0) continue;
+      const u32x4* row = y + int64_t(src) * hv;
+      u32x4 v[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        v[u] = c < hv ? row[c] : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[u][2 * q] = fmaf(g, bf16_lo(v[u][q]), acc[u][2 * q]);
+          acc[u][2 * q + 1] = fmaf(g, bf16_hi(v[u][q]), acc[u][2 * q + 1]);
+        }
+      }
+    }
+    u32x4* o = out + int64_t(t) * hv;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < hv) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
+        o[c] = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// reduce_grad: grid (chunks, E); y-block i handles the i-th expert that has
+// consumers.  Its consumers are the CSR entries of its moves, already in
+// ascending receiver rank; entries with b >= B (inference overflow) own no
+// slot and are skipped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_reduce_grad(f32x4* __restrict__ grad_home,
+                                                     f32x4* __restrict__ grad_pref,
+                                                     const int32_t* __restrict__ cons,
+                                                     const int32_t* __restrict__ misc,
+                                                     const int32_t* __restrict__ mptr,
+                                                     const int32_t* __restrict__ mcnt,
+                                                     const int32_t* __restrict__ cs_dst,
+                                                     const int32_t* __restrict__ cs_b, int B,
+                                                     int64_t nvec) {
+  __shared__ int s_slot[MOE_MAX_R];
+  __shared__ int s_n;
+  if ((int)blockIdx.y >= misc[0]) return;
+  const int e = cons[blockIdx.y];
+  if (threadIdx.x == 0) {
+    int k = 0;
+    const int q0 = mptr[e], q1 = q0 + mcnt[e];
+    for (int q = q0; q < q1; ++q) {
+      const int b = cs_b[q];
+      if (b < B && k < MOE_MAX_R) s_slot[k++] = cs_dst[q] * B + b;
+    }
+    s_n = k;
+  }
+  __syncthreads();
+  const int ns = s_n;
+  if (ns == 0) return;
+  f32x4* home = grad_home + int64_t(e) * nvec;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+    f32x4 acc = home[v];
+    for (int s = 0; s < ns; ++s) {
+      f32x4* p = grad_pref + int64_t(s_slot[s]) * nvec + v;
+      const f32x4 g = *p;
+      acc.x += g.x;
+      acc.y += g.y;
+      acc.z += g.z;
+      acc.w += g.w;
+      *p = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    home[v] = acc;
+  }
+}
+
+}  // namespace moonep
+
+using namespace moonep;
+
+extern "C" int moe_prefetch_weight(const moe_cfg* cfg, const moe_plan* plan,
+                                   const moe_bf16* w_home, moe_bf16* w_pref, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!plan || !plan->slot_expert) return MOE_EINVAL;
+  const int64_t RB = int64_t(cfg->R) * cfg->B;
+  if (RB == 0) return MOE_OK;
+  if (!w_home || !w_pref) return MOE_EINVAL;
+  const int64_t nvec = int64_t(cfg->H) * cfg->Hp / 8;
+  int chunks = (int)std::min<int64_t>(64, (nvec + 256 * 16 - 1) / (256 * 16));
+  if (chunks < 1) chunks = 1;
+  hipLaunchKernelGGL(k_prefetch, dim3(chunks, (unsigned)RB), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(w_home), reinterpret_cast<u32x4*>(w_pref),
+                     plan->slot_expert, nvec);
+  return hip_status();
+}
+
+extern "C" int moe_dispatch(const moe_cfg* cfg, const moe_plan* plan, const moe_bf16* x,
+                            moe_bf16* xperm, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  const int ntok = cfg->R * cfg->S;
+  if (ntok == 0) return MOE_OK;
+  if (!plan || !plan->route || !x || !xperm) return MOE_EINVAL;
+  const int hv = cfg->H / 8;
+  const int du = (hv + kWave - 1) / kWave;
+  const dim3 grid((ntok + 3) / 4), block(256);
+  const u32x4* xs = reinterpret_cast<const u32x4*>(x);
+  u32x4* xd = reinterpret_cast<u32x4*>(xperm);
+#define MOE_DISPATCH(N)                                                                      \
+  hipLaunchKernelGGL(k_dispatch<N>, grid, block, 0, stream, xs, xd, plan->route, ntok, cfg->K, \
+                     hv)
+  if (du <= 1) MOE_DISPATCH(1);
+  else if (du <= 2) MOE_DISPATCH(2);
+  else if (du <= 4) MOE_DISPATCH(4);
+  else if (du <= 8) MOE_DISPATCH(8);
+  else if (du <= 14) MOE_DISPATCH(14);
+  else MOE_DISPATCH(16);
+#undef MOE_DISPATCH
+  return hip_status();
+}
+
+extern "C" int moe_combine(const moe_cfg* cfg, const moe_plan* plan, const moe_bf16* y,
+                           const float* gates, moe_bf16* out, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  const int ntok = cfg->R * cfg->S;
+  if (ntok == 0) return MOE_OK;
+  if (!plan || !plan->route || !y || !gates || !out) return MOE_EINVAL;
+  const int hv = cfg->Hp / 8;
+  const int cu = (hv + kWave - 1) / kWave;
+  const dim3 grid((ntok + 3) / 4), block(256);
+  const u32x4* ys = reinterpret_cast<const u32x4*>(y);
+  u32x4* od = reinterpret_cast<u32x4*>(out);
+#define MOE_COMBINE(N)                                                                        \
+  hipLaunchKernelGGL(k_combine<N>, grid, block, 0, stream, ys, gates, plan->route, od, ntok, \
+                     cfg->K, hv)
+  if (cu <= 1) MOE_COMBINE(1);
+  else if (cu <= 2) MOE_COMBINE(2);
+  else MOE_COMBINE(4);
+#undef MOE_COMBINE
+  return hip_status();
+}
+
+extern "C" int moe_reduce_grad(const moe_cfg* cfg, const moe_plan* plan, float* grad_home,
+                               float* grad_pref, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!plan || !plan->workspace) return MOE_EINVAL;
+  if (cfg->B == 0) return MOE_OK;
+  if (!grad_home || !grad_pref) return MOE_EINVAL;
+  if ((int64_t(cfg->H) * cfg->Hp) % 4 != 0) return MOE_EINVAL;
+  const PlanLayout L = plan_layout(cfg);
+  void* ws = plan->workspace;
+  const int64_t nvec = int64_t(cfg->H) * cfg->Hp / 4;
+  int chunks = (int)std::min<int64_t>(128, (nvec + 256 * 8 - 1) / (256 * 8));
+  if (chunks < 1) chunks = 1;
+  hipLaunchKernelGGL(k_reduce_grad, dim3(chunks, cfg->E), dim3(256), 0, stream,
+                     reinterpret_cast<f32x4*>(grad_home), reinterpret_cast<f32x4*>(grad_pref),
+                     ws_i32(ws, L.off_cons), ws_i32(ws, L.off_misc), ws_i32(ws, L.off_mptr),
+                     ws_i32(ws, L.off_mcnt), ws_i32(ws, L.off_cs_dst), ws_i32(ws, L.off_cs_b),
+                     cfg->B, nvec);
+  return hip_status();
+}

@@ -1,0 +1,88 @@
+"""The C-ABI library loads and exports every symbol include/*.h declares.
+
+CPU only: no call here touches a GPU (only the host-only size and error-text
+entry points are called).
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_expert_load_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _ensure_built():
+    if not os.path.exists(mx.LIB_PATH):
+        from moe_expert_load_amd import build
+        build.build()
+
+
+def declared_entry_points():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\**\s*(moe_\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = declared_entry_points()
+    assert names == set(mx.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    _ensure_built()
+    lib = ctypes.CDLL(mx.LIB_PATH)
+    for name in declared_entry_points():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mx.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert declared_entry_points() <= exported
+
+
+def test_host_only_calls_and_validation():
+    _ensure_built()
+    cfg = mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 48)
+    sizes = mx.moe_plan_sizes(cfg)
+    assert sizes[0] == 4 * 384 and sizes[1] == 4 * 8
+    assert sizes[2] == 4 * 8 * 8192 * 8
+    assert sizes[3] == 4 * 8 * (384 + 48 + 1)
+    assert sizes[7] == 16 * (384 + 8 - 1) and sizes[8] == 16
+    assert sizes[9] > 0
+    assert mx.moe_gemm_workspace_size(cfg) > 0
+    bad = [
+        mx.make_cfg(8, 16, 30, 2, 128, 64, 3),            # E % R != 0
+        mx.make_cfg(4, 16, 8, 9, 128, 64, 2),             # K > E
+        mx.make_cfg(4, 16, 8, 2, 128, 64, 1),             # train needs B = E/R
+        mx.make_cfg(4, 16, 8, 2, 128, 64, 3, mx.MODE_INFER),  # B > E/R
+        mx.make_cfg(4, 16, 8, 2, 100, 64, 2),             # H % 8 != 0
+        mx.make_cfg(4, 16, 8, 2, 128, 64, 2, 7),          # bad mode
+    ]
+    for c in bad:
+        with pytest.raises(mx.MoeError) as ei:
+            mx.moe_plan_sizes(c)
+        assert ei.value.code == mx.MOE_EINVAL
+    with pytest.raises(mx.MoeError) as ei:
+        mx.moe_plan_sizes(mx.make_cfg(4, 16, 4096, 2, 128, 64, 1024))
+    assert ei.value.code == mx.MOE_ELIMIT
+    with pytest.raises(mx.MoeError) as ei:
+        mx.moe_plan_sizes(mx.make_cfg(64, 1 << 20, 896, 64, 128, 64, 14))
+    assert ei.value.code == mx.MOE_ELIMIT
+    # inference may use fewer slots, even none
+    mx.moe_plan_sizes(mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 4, mx.MODE_INFER))
+    mx.moe_plan_sizes(mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 0, mx.MODE_INFER))
+    assert mx.moe_strerror(mx.MOE_EINVAL).startswith("invalid")
+    assert mx.moe_strerror(12345) == "unknown error code"
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        mx.load(str(tmp_path / "nope.so"))

@@ -1,0 +1,120 @@
+"""GPU parity of moe_plan_run against the oracle: bit-exact, every output.
+
+Runs through the C-ABI binding.  Shapes: the tiny shape over many seeds,
+edge shapes, the skewed and bench maxvio sweeps (shared seed), the Large-E
+shape, the Theorem-2 worst case in train and inference mode, maximum skew,
+and out-of-range ids (status bit, route -1).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_load_amd as mx
+import workloads as W
+from gpu_helpers import announce, assert_plan_equal, cfgs, free, gpu_plan
+from oracle.plan import make_plan
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    free()
+
+
+def check(shape, ids, plan=None):
+    announce("plan", shape.name, shape)
+    _, oc = cfgs(shape)
+    ref = make_plan(ids, oc)
+    plan, g = gpu_plan(shape, ids, plan)
+    assert_plan_equal(g, ref, shape)
+    return plan, g, ref
+
+
+def test_tiny_many_seeds():
+    plan = None
+    for seed in range(300):
+        ids, _ = W.routing_uniform(W.TINY, salt=seed)
+        plan, _, _ = check(W.TINY, ids, plan)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(R=1, B=8), dict(K=8), dict(R=8, E=8, B=1), dict(S=1), dict(S=3, K=5),
+    dict(B=0, mode=1), dict(B=1, mode=1), dict(R=64, E=128, S=5, K=3, B=2),
+    dict(R=3, E=9, S=7, K=3, B=3), dict(R=16, E=64, S=33, K=7, B=4),
+    dict(E=512, R=4, S=40, K=16, B=128), dict(E=2048, R=8, S=20, K=64, B=256),
+    dict(R=1024, E=1024, S=2, K=2, B=1), dict(R=5, E=1000, S=77, K=9, B=200)])
+def test_edge_shapes(kw):
+    shape = W.TINY.with_(**kw)
+    for seed in range(6):
+        if seed == 5:
+            ids = W.routing_hot(shape)
+        elif seed == 4 and shape.R > 1:
+            ids = W.routing_theorem2(shape)
+        else:
+            ids, _ = W.routing_uniform(shape, salt=seed)
+        check(shape, ids)
+
+
+def test_empty_tokens():
+    shape = W.TINY.with_(S=0)
+    c, _ = cfgs(shape)
+    plan = mx.Plan(c)
+    mx.moe_plan_run(c, torch.zeros(0, dtype=torch.int32, device="cuda"), plan)
+    v = {k: t.cpu().numpy() for k, t in plan.views().items()}
+    assert np.all(v["cu_seqlens"] == 0) and np.all(v["counts"] == 0)
+    assert list(v["status"][:3]) == [0, 0, 0]
+
+
+@pytest.mark.parametrize("name", ["skewed", "bench"])
+def test_maxvio_sweep(name):
+    shape = W.SHAPES[name]
+    plan = None
+    for target in W.MAXVIO_SWEEP[name]:
+        ids, _, _, mv = W.routing_zipf(shape, target)
+        announce("sweep", name, target, "maxvio", mv)
+        plan, g, ref = check(shape, ids, plan)
+        assert np.all(np.bincount(g["route"] // shape.SK, minlength=shape.R) == shape.SK)
+        assert g["n_redundant"].max() <= shape.n
+        # determinism: a second run is bit-identical
+        plan, g2 = gpu_plan(shape, ids, plan)
+        for k in g:
+            assert np.array_equal(g[k], g2[k]), k
+
+
+def test_large_e():
+    shape = W.LARGE_E
+    for target in W.MAXVIO_SWEEP["large_e"]:
+        ids, _, _, mv = W.routing_zipf(shape, target)
+        announce("large_e", target, mv)
+        check(shape, ids)
+    _, g, _ = check(shape, W.routing_theorem2(shape))
+    assert g["n_redundant"].max() == 14
+
+
+@pytest.mark.parametrize("shape", [W.ADVERSARIAL, W.ADVERSARIAL_INFER])
+def test_theorem2_worst_case(shape):
+    _, g, ref = check(shape, W.routing_theorem2(shape))
+    assert list(g["n_redundant"]) == [42, 36, 30, 24, 18, 12, 6, 0]
+    if shape.mode == 1:
+        assert (g["slot_expert"] >= 0).sum(axis=1).max() == shape.B
+
+
+def test_bad_ids_set_status_and_route():
+    shape = W.TINY
+    ids, _ = W.routing_uniform(shape, salt=3)
+    ids = ids.copy()
+    ids[5, 1] = shape.E + 3
+    ids[9, 0] = -1
+    announce("bad ids")
+    _, g = gpu_plan(shape, ids)
+    assert g["status"][2] & mx.STATUS_BAD_ID
+    assert np.all(g["route"] == -1)
+    assert np.all(g["cu_seqlens"] == 0)
+    assert np.all(g["slot_expert"] == -1)
+    # counts exclude the bad slots
+    good = ids.reshape(-1)
+    good = good[(good >= 0) & (good < shape.E)]
+    assert np.array_equal(g["counts"], np.bincount(good, minlength=shape.E))
