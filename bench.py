@@ -1,0 +1,328 @@
+"""Benchmark of the MoonEP hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input at
+the bench shape (R=8 virtual ranks, S=8192 tokens/rank, E=384, K=8,
+H=7168, H'=2048, B=E/R=48, bf16, Zipf-biased routing tuned to maxvio 1):
+
+    plan -> prefetch_weight -> dispatch -> grouped GEMM (all 8 ranks, one
+    launch) -> combine -> weight-grad GEMM -> reduce_grad
+
+All inputs are resident in HBM before timing starts.  W untimed warmup
+steps, then K timed steps bracketed by device synchronisation; every entry
+point is also bracketed by HIP events on the stream it runs on, giving each
+step's average duration.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
+                    [--sweep] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_expert_load_amd as mx  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "plan µs + dispatch/combine GB/s + grouped-GEMM TFLOP/s @S8192 E384 K8 R8"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+STEPS = ("plan", "prefetch", "dispatch", "gemm", "combine", "wgrad", "reduce_grad")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Path:
+    """Buffers and calls of one layer at one shape."""
+
+    def __init__(self, shape, ids, gates, seed=0):
+        self.shape = s = shape
+        self.c = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
+        dev = "cuda"
+        self.ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
+        self.gates = torch.from_numpy(np.ascontiguousarray(gates, np.float32)).to(dev)
+        self.plan = mx.Plan(self.c, dev)
+        self.x = W.randn_bf16((s.tokens, s.H), seed + 1, dev)
+        self.w_home = W.randn_bf16((s.E, s.H, s.Hp), seed + 2, dev, chunk_rows=1)
+        self.dy = W.randn_bf16((s.R * s.SK, s.Hp), seed + 3, dev)
+        self.w_pref = torch.empty((s.R * s.B, s.H, s.Hp), dtype=torch.bfloat16, device=dev)
+        self.xperm = torch.empty((s.R * s.SK, s.H), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((s.R * s.SK, s.Hp), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((s.tokens, s.Hp), dtype=torch.bfloat16, device=dev)
+        self.gh = torch.zeros((s.E, s.H, s.Hp), dtype=torch.float32, device=dev)
+        self.gp = torch.zeros((s.R * s.B, s.H, s.Hp), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(mx.moe_gemm_workspace_size(self.c), dtype=torch.uint8, device=dev)
+
+    def calls(self):
+        c, p = self.c, self.plan
+        return (
+            ("plan", lambda: mx.moe_plan_run(c, self.ids, p)),
+            ("prefetch", lambda: mx.moe_prefetch_weight(c, p, self.w_home, self.w_pref)),
+            ("dispatch", lambda: mx.moe_dispatch(c, p, self.x, self.xperm)),
+            ("gemm", lambda: mx.moe_grouped_gemm(c, self.xperm, self.w_home, self.w_pref,
+                                                 p.cu_seqlens, self.y, 0, self.shape.R, self.ws)),
+            ("combine", lambda: mx.moe_combine(c, p, self.y, self.gates, self.out)),
+            ("wgrad", lambda: mx.moe_grouped_gemm_wgrad(c, p, self.xperm, self.dy, self.gh,
+                                                        self.gp, self.ws)),
+            ("reduce_grad", lambda: mx.moe_reduce_grad(c, p, self.gh, self.gp)),
+        )
+
+    def run(self, steps, timed, only=None):
+        calls = [(n, f) for n, f in self.calls() if only is None or n in only]
+        ev = []
+        for _ in range(steps):
+            row = []
+            for name, f in calls:
+                if timed:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    f()
+                    b.record()
+                    row.append((name, a, b))
+                else:
+                    f()
+            ev.append(row)
+        return ev
+
+
+def work_units(shape, plan_views):
+    """Algorithmic bytes / flops of each step (what the method must move)."""
+    s = shape
+    H, Hp, K, T = s.H, s.Hp, s.K, s.tokens
+    slot_expert = plan_views["slot_expert"].cpu().numpy()
+    n_slots = int((slot_expert >= 0).sum())
+    n_cons = int(len(np.unique(slot_expert[slot_expert >= 0])))
+    rows = s.R * s.SK
+    return {
+        "plan": ("bytes", 8.0 * rows),                       # read id, write route
+        "prefetch": ("bytes", 2.0 * 2 * H * Hp * n_slots),   # read + write each slot
+        "dispatch": ("bytes", float(T) * (2 * H * (1 + K) + 4 * K)),
+        "gemm": ("flops", 2.0 * H * Hp * rows),
+        "combine": ("bytes", float(T) * (2 * Hp * (K + 1) + 8 * K)),
+        "wgrad": ("flops", 2.0 * H * Hp * rows),
+        "reduce_grad": ("bytes", 8.0 * H * Hp * (n_slots + n_cons)),
+    }, {"slots": n_slots, "experts_with_slots": n_cons}
+
+
+def cpu_baseline(shape, ids, gates, path, budget_s=25.0):
+    """The oracle on the host cores, on a bounded sample, scaled to a step."""
+    from threadpoolctl import threadpool_info
+    from oracle import bf16, dataflow
+    from oracle.plan import Cfg, make_plan
+
+    s = shape
+    oc = Cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    ref = make_plan(ids, oc)
+    t_plan = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    # dispatch: 2048 tokens, their K rows (the oracle's fancy-index bit copy)
+    toks = np.sort(rng.choice(s.tokens, 2048, replace=False))
+    xb = W.bf16_bits(path.x.index_select(0, torch.as_tensor(toks, device="cuda")))
+    slots = (toks[:, None] * s.K + np.arange(s.K)[None]).reshape(-1)
+    t0 = time.perf_counter()
+    dst = np.argsort(np.argsort(ref.route[slots]))
+    buf = np.zeros((len(slots), s.H), np.uint16)
+    buf[dst] = xb[np.arange(len(slots)) // s.K]
+    t_disp = (time.perf_counter() - t0) * s.tokens / len(toks)
+    # grouped GEMM: oracle gemm_rows on 4 segments x 128 rows; weight
+    # conversion is extrapolated per active segment, the product per row
+    nz = [(r, int(j)) for r in range(s.R) for j in np.nonzero(ref.seg_len[r])[0]]
+    pick = [nz[i] for i in rng.choice(len(nz), 4, replace=False)]
+    wr = _DevRows(path.w_home)
+    xr = _DevRows(path.x)
+    t0 = time.perf_counter()
+    bf16.bits_to_f64(wr[0])
+    t_conv = time.perf_counter() - t0
+    rows = np.concatenate([s.SK * r + ref.cu_seqlens[r, j] +
+                           np.arange(min(128, ref.seg_len[r, j])) for r, j in pick])
+    t0 = time.perf_counter()
+    dataflow.gemm_rows(rows, xr, wr, _OraclePref(wr, ref), ref, oc)
+    t_rows = time.perf_counter() - t0
+    nseg = len(nz)
+    t_gemm = t_conv * nseg + max(t_rows - 4 * t_conv, 0.0) / len(rows) * (s.R * s.SK)
+    # combine: 2048 tokens from synthetic y rows
+    yrows = rng.integers(0, 2 ** 15, (len(toks) * s.K, s.Hp)).astype(np.uint16)
+    t0 = time.perf_counter()
+    acc = np.zeros((len(toks), s.Hp))
+    for k in range(s.K):
+        acc += gates[toks, k:k + 1].astype(np.float64) * bf16.bits_to_f64(yrows[k::s.K])
+    bf16.f64_to_bits(acc)
+    t_comb = (time.perf_counter() - t0) * s.tokens / len(toks)
+    # weight-grad GEMM: same float64 rate as the forward product (same flops)
+    t_wgrad = t_gemm
+    # reduce_grad: 1/64 of one expert row, scaled to every consumed slot
+    n = s.H * s.Hp // 64
+    hrow = rng.standard_normal(n)
+    prow = rng.standard_normal((2, n))
+    t0 = time.perf_counter()
+    hrow = hrow + prow[0] + prow[1]
+    prow[:] = 0
+    t_red1 = (time.perf_counter() - t0) / 2 * 64
+    n_slots = int((ref.slot_expert >= 0).sum())
+    t_red = t_red1 * n_slots
+    total = t_plan + t_disp + t_gemm + t_comb + t_wgrad + t_red
+    return {
+        "value": s.tokens / total,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": ("oracle on host: plan at full size (%.2fs); dispatch and combine on 2048 of "
+                   "%d tokens; GEMM via oracle gemm_rows on 4 segments x <=128 rows, weight "
+                   "conversion extrapolated to %d segments and the float64 product per row "
+                   "(fwd and wgrad %.0fs each, extrapolated); reduce_grad on 1/64 of a slot, "
+                   "scaled to %d slots; step total %.1fs extrapolated"
+                   % (t_plan, s.tokens, nseg, t_gemm, n_slots, total)),
+        "seconds": {"plan": t_plan, "dispatch": t_disp, "gemm": t_gemm, "combine": t_comb,
+                    "wgrad": t_wgrad, "reduce_grad": t_red},
+        "host_cpus": {"affinity": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()},
+    }
+
+
+class _OraclePref:
+    def __init__(self, w, plan):
+        self.w, self.plan = w, plan
+
+    def __getitem__(self, rb):
+        return self.w[int(self.plan.slot_expert[rb[0], rb[1]])]
+
+
+class _DevRows:
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, i):
+        if np.isscalar(i):
+            return W.bf16_bits(self.t[int(i)])
+        return W.bf16_bits(self.t.index_select(0, torch.as_tensor(np.asarray(i), device="cuda")))
+
+
+def measure(path, steps, warmup):
+    path.run(warmup, timed=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev = path.run(steps, timed=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in STEPS}
+    for row in ev:
+        for name, a, b in row:
+            per[name].append(a.elapsed_time(b))
+    ms = {n: float(np.mean(v)) for n, v in per.items() if v}
+    span = ev[0][0][1].elapsed_time(ev[-1][-1][2])
+    return ms, span / steps, wall / steps * 1e3
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--maxvio", type=float, default=1.0)
+    ap.add_argument("--sweep", action="store_true", help="also time plan/dispatch/gemm/combine "
+                    "at every maxvio of the sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the R expert-parallel ranks are virtual ranks "
+              "inside one GPU's memory; --gpus %d is not supported" % args.gpus)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mx.load()
+    shape = W.BENCH
+    log("routing: zipf maxvio target", args.maxvio)
+    ids, gates, s_bias, mv = W.routing_zipf(shape, args.maxvio)
+    log("allocating and generating inputs")
+    path = Path(shape, ids, gates)
+    torch.cuda.synchronize()
+    log("warmup + timed steps")
+    ms, span_ms, wall_ms = measure(path, args.steps, args.warmup)
+    st = path.plan.views()["status"].cpu().numpy()
+    if st[2] != 0:
+        raise RuntimeError("plan status bits %d" % st[2])
+    units, plan_stats = work_units(shape, path.plan.views())
+    comps = {}
+    roof = []
+    for name in STEPS:
+        kind, amount = units[name]
+        t = ms[name] * 1e-3
+        if kind == "flops":
+            ach = amount / t / 1e12
+            roof.append({"step": name, "bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "ms": ms[name]})
+            comps[name + "_TFLOPs"] = ach
+        else:
+            ach = amount / t / 1e9
+            bound = "latency" if name == "plan" else "hbm"
+            roof.append({"step": name, "bound": bound, "achieved": ach, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "ms": ms[name]})
+            comps[name + "_GBps"] = ach
+    comps["plan_us"] = ms["plan"] * 1e3
+    dom = max((r for r in roof if r["step"] != "plan"), key=lambda r: r["ms"])
+    kernel_of = {"gemm": "k_gemm<0> (grouped GEMM, 256x256 MFMA tiles)",
+                 "wgrad": "k_gemm<1> (weight-grad GEMM)",
+                 "dispatch": "k_dispatch", "combine": "k_combine",
+                 "prefetch": "k_prefetch", "reduce_grad": "k_reduce_grad"}
+    gemm_units = units[dom["step"]][1]
+    roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                "unit": dom["unit"], "frac": dom["frac"], "traffic": None,
+                "kernel": kernel_of[dom["step"]],
+                "algorithmic_per_launch": gemm_units, "avg_launch_ms": dom["ms"]}
+    line = {
+        "metric": METRIC,
+        "value": shape.tokens / (span_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": span_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bench shape: R=8 virtual ranks, S=8192 tokens/rank, E=384, K=8, "
+                               "H=7168, H'=2048, B=48, train mode, zipf routing maxvio %.3f" % mv,
+                   "R": shape.R, "S": shape.S, "E": shape.E, "K": shape.K, "H": shape.H,
+                   "Hp": shape.Hp, "B": shape.B, "maxvio": mv, "zipf_s": s_bias,
+                   "redundant_slots": plan_stats["slots"]},
+        "components": comps,
+        "step_ms": ms,
+        "wall_ms_per_step": wall_ms,
+        "roofline": roofline,
+        "rooflines": roof,
+    }
+    if args.sweep:
+        sweep = {}
+        for t in W.MAXVIO_SWEEP["bench"]:
+            ids2, gates2, _, mv2 = W.routing_zipf(shape, t)
+            path.ids = torch.from_numpy(np.ascontiguousarray(ids2, np.int32)).cuda()
+            path.gates = torch.from_numpy(gates2).cuda()
+            m2, _, _ = measure(path, max(3, args.steps // 2), 2)
+            u2, st2 = work_units(shape, path.plan.views())
+            sweep["%.1f" % t] = {
+                "maxvio": mv2, "plan_us": m2["plan"] * 1e3,
+                "dispatch_GBps": u2["dispatch"][1] / m2["dispatch"] / 1e6,
+                "combine_GBps": u2["combine"][1] / m2["combine"] / 1e6,
+                "gemm_TFLOPs": u2["gemm"][1] / m2["gemm"] / 1e9,
+                "redundant_slots": st2["slots"]}
+            log("sweep", t, sweep["%.1f" % t])
+        line["maxvio_sweep"] = sweep
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host, bounded sample)")
+        line["cpu_baseline"] = cpu_baseline(shape, ids, gates, path)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,7 @@
 // gradient) are loaded as 8x8 bf16 blocks and transposed in registers
 // before the LDS store.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "host.hpp"
@@ -32,12 +33,13 @@ namespace moonep {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
 constexpr int kGemmThreads = 256;
-constexpr int kTileBytes = BM * BK * 2;          // 32 KB per operand tile
-constexpr int kCRow = 272;                        // epilogue row pitch (bytes)
-constexpr int kGemmLds = 4 * 128 * kCRow;         // >= A and B double buffered (128 KB)
 
 enum { MODE_FWD = 0, MODE_WGRAD = 1 };
 
@@ -58,35 +60,131 @@ struct GemmArgs {
   int32_t H, Hp, E, B, SK;
 };
 
-// Byte offset of 16-byte chunk kc of row `row` in a [256][64] bf16 LDS tile.
-__device__ __forceinline__ int lds_off(int row, int kc) {
-  return row * (BK * 2) + ((kc ^ ((row >> 1) & 7)) << 4);
+// Range-checked buffer resource over [base, base + bytes): loads past the end
+// return zeros (per dword), which pads ragged row/K tails with zeros.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{uint32_t(b), uint32_t(b >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-// Column c of an 8x8 bf16 block held as 8 rows (one u32x4 per row): the 8
-// values in[0..7][c], packed two per dword.
-__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&in)[8], int c) {
-  u32x4 out;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t a = in[2 * d][c >> 1], b = in[2 * d + 1][c >> 1];
-    out[d] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-  }
-  return out;
+// 16 bytes per lane from global memory straight into LDS (buffer_load ...
+// lds): lane l writes lds_dst + 16*l; lds_dst must be wave-uniform.  Issued
+// as inline assembly so the compiler does not pair every later LDS read with
+// a wait for all such loads; the kernel waits for each stage itself
+// (wait_vm) before the barrier that publishes it.
+__device__ __forceinline__ void load_lds16(u32x4 rsrc, const unsigned char* lds_dst,
+                                           uint32_t voff, uint32_t soff) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)lds_dst;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(l), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Transposing LDS read: the 16 lanes of a group each name a 64-bit piece
+// (4 bf16) of a 4-row x 16-column block; lane (a, c) = (i/4, i%4) receives
+// column 4a + c of rows 0..3.  Used so that an operand stored [k][col] in
+// LDS arrives as 8 consecutive k per lane, the MFMA layout.
+__device__ __forceinline__ u32x2 lds_tr(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ bf16x8 join(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Pipeline: BK = 32 deep stages, 4 of them.  Each stage's two operand
+// tiles are separate LDS arrays so the compiler can tell a read of one stage
+// from the in-flight direct loads of the others and wait only for the
+// stage it reads.
+constexpr int kBK = 32;
+constexpr int kNST = 4;
+constexpr int kTile = 256 * kBK * 2;             // 16 KB per operand tile
+__shared__ __attribute__((aligned(1024))) unsigned char g_sa0[kTile], g_sb0[kTile];
+__shared__ __attribute__((aligned(1024))) unsigned char g_sa1[kTile], g_sb1[kTile];
+__shared__ __attribute__((aligned(1024))) unsigned char g_sa2[kTile], g_sb2[kTile];
+__shared__ __attribute__((aligned(1024))) unsigned char g_sa3[kTile], g_sb3[kTile];
+
+template <int S>
+__device__ __forceinline__ unsigned char* stage_a() {
+  if constexpr (S == 0) return g_sa0;
+  else if constexpr (S == 1) return g_sa1;
+  else if constexpr (S == 2) return g_sa2;
+  else return g_sa3;
+}
+template <int S>
+__device__ __forceinline__ unsigned char* stage_b() {
+  if constexpr (S == 0) return g_sb0;
+  else if constexpr (S == 1) return g_sb1;
+  else if constexpr (S == 2) return g_sb2;
+  else return g_sb3;
+}
+
+// Workgroup barrier that orders this wave's LDS accesses around it but does
+// not wait for outstanding global loads (the direct-to-LDS loads of later
+// stages stay in flight; each wave waits for its own with wait_vm first).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+// Tiles of one pipeline stage:
+//  * "row tile" [256 rows][32 k] (forward A, k contiguous): 16-byte chunk kc
+//    of row m is stored at chunk kc ^ ((m >> 2) & 3), so 16 consecutive rows
+//    reading one chunk hit 64 distinct banks;
+//  * "col tile" [32 k][256 cols] (weights, dy, and x^T in the weight
+//    gradient; columns contiguous): chunk c of row k is stored at
+//    c ^ (4 * (k % 4)), so a transposing read of 4 rows x 4 chunks per 32
+//    lanes is conflict free.
+// Both are filled by buffer_load ... lds in whole 1 KB wave instructions;
+// each lane fetches the global chunk whose swizzled position is its slot.
+template <int MODE>
+struct GemmTile {
+  static constexpr int BK = kBK;
+  static constexpr int ROWB = BK * 2;          // bytes per row-tile row
+  static constexpr int CPR = BK / 8;           // 16-byte chunks per row-tile row
+  static constexpr int RSH = 2;                // rows per 256 bytes = 1 << RSH
+  static constexpr int NI = kTile / 1024 / 4;  // 1 KB loads per wave per operand
+  static constexpr int RPI = 1024 / ROWB;      // row-tile rows per load
+};
 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  using T = GemmTile<MODE>;
+  constexpr int BK = T::BK, ROWB = T::ROWB, CPR = T::CPR, RSH = T::RSH, NI = T::NI;
+  static_assert(NI == 4 && CPR == 4, "tile geometry");
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wv >> 1, wn = wv & 1;
   const int H = g.H, Hp = g.Hp;
-  const int MDIM = MODE == MODE_FWD ? 0 : H;     // wgrad: output rows are h
-  const int ntm = MODE == MODE_FWD ? 1 : (MDIM + BM - 1) / BM;
+  const int ntm = MODE == MODE_FWD ? 1 : (H + BM - 1) / BM;
   const int ntn = (Hp + BN - 1) / BN;
   const int64_t total = int64_t(*g.nitems) * ntm * ntn;
   const int G = gridDim.x, per = G / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+
+  // Per-lane pieces of the transposing reads (col tiles), see lds_tr:
+  // G4 = lane/16 picks the k half (G4/2) and the column half (G4%2).
+  const int G4 = lane >> 4, li = lane & 15;
+  const int tr_k = 8 * (G4 >> 1) + (li >> 2);            // + 16 s + 4 h
+  int tr_off[4];                                          // per 32-column block
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = (4 * j + 2 * (G4 & 1) + ((li & 3) >> 1)) ^ (4 * (li >> 2));
+    tr_off[j] = tr_k * 512 + c * 16 + 8 * (li & 1);
+  }
+  // Row-tile MFMA reads (forward A): row = wm*128 + 32 i + lane%32,
+  // chunk 2 s + lane/32.
+  int ra_off[BK / 16];
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+    const int row = lane & 31, kc = 2 * s + (lane >> 5);
+    ra_off[s] = (wm * 128 + row) * ROWB + ((kc ^ ((row >> RSH) & (CPR - 1))) << 4);
+  }
 
   for (int64_t q = 0;; ++q) {
     const int64_t w = q * G + int64_t(xcd) * per + local;
@@ -95,34 +193,45 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     const int rest = (int)(w % (ntm * ntn));
     const int tm = rest / ntn, tn = rest % ntn;
     const WorkItem it = g.items[item];
-    const int n0 = tn * BN;
-    const int m0 = tm * BM;  // wgrad: first h of the tile
-    // K extent: H for the forward, the segment length for the wgrad
+    const int n0 = tn * BN, m0 = tm * BM;
     const int KD = MODE == MODE_FWD ? H : it.rows;
     const int nk = (KD + BK - 1) / BK;
 
-    // Uniform (scalar) bases plus 32-bit per-lane element offsets, so the
-    // loads use scalar-base addressing and few vector registers.
-    const uint16_t* Ab = g.xperm + int64_t(it.row0) * H;
-    const uint16_t* Bb;
-    if (MODE == MODE_FWD)
-      Bb = it.j < g.E ? g.w_home + int64_t(it.j) * H * Hp
-                      : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
-    else
-      Bb = g.dy + int64_t(it.row0) * Hp;
-    const int kg = tid & 7, cg = tid >> 3;   // 8x8 block: k group, column group
-    // forward A: rows cg + 32i (masked to the segment), chunk kg
-    uint32_t aoff = 0;
-    int arow_lim = 0;
+    // Operand A: forward = xperm rows of the segment (row tile); weight
+    // gradient = the same rows read as x^T (col tile over h).
+    // Operand B: forward = weight W(r, j) [H][Hp]; weight gradient = dy rows.
+    const uint16_t* Abase = g.xperm + int64_t(it.row0) * H;
+    const uint16_t* Bbase;
+    uint32_t bbytes;
     if (MODE == MODE_FWD) {
-      aoff = uint32_t(cg) * H + kg * 8;
-      arow_lim = it.rows - cg;               // row cg + 32i valid iff 32i < arow_lim
+      Bbase = it.j < g.E ? g.w_home + int64_t(it.j) * H * Hp
+                         : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
+      bbytes = uint32_t(H) * Hp * 2;
     } else {
-      aoff = uint32_t(kg * 8) * H + m0 + cg * 8;
+      Bbase = g.dy + int64_t(it.row0) * Hp;
+      bbytes = uint32_t(it.rows) * Hp * 2;
     }
-    const uint32_t boff = uint32_t(kg * 8) * Hp + n0 + cg * 8;
-    const bool bcol_ok = n0 + cg * 8 < Hp;
-    const bool acol_ok = MODE == MODE_FWD ? true : (m0 + cg * 8 < H);
+    const u32x4 ra = make_rsrc(Abase, uint32_t(it.rows) * H * 2);
+    const u32x4 rb = make_rsrc(Bbase, bbytes);
+
+    // Per-lane global byte offsets of this wave's load instructions.
+    uint32_t goa[NI], gob[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int t = wv * NI + u;
+      if (MODE == MODE_FWD) {
+        const int row = t * T::RPI + lane / CPR;
+        const int kc = (lane % CPR) ^ ((row >> RSH) & (CPR - 1));
+        goa[u] = uint32_t(row) * H * 2 + kc * 16;
+      } else {
+        const int row = t * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ (4 * (row & 3));
+        goa[u] = uint32_t(row) * H * 2 + uint32_t(m0 + 8 * c) * 2;
+      }
+      const int row = t * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 3));
+      gob[u] = uint32_t(row) * Hp * 2 + uint32_t(n0 + 8 * c) * 2;
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -132,127 +241,120 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    u32x4 ra[8], rb[8];
-    const u32x4 zero4 = {0, 0, 0, 0};
-    // Global -> registers for k-tile kt.
-    auto load = [&](int kt) {
-      const int k0 = kt * BK;
-      if (MODE == MODE_FWD) {
-        const uint16_t* a = Ab + k0;
-        const bool kok = k0 + kg * 8 < H;
+    // Direct loads of k-tile kt into stage S (= kt % 4).
+    auto issue = [&](auto S_, int kt) {
+      constexpr int S = decltype(S_)::value;
+      unsigned char* As = stage_a<S>();
+      unsigned char* Bs = stage_b<S>();
+      const uint32_t ka = MODE == MODE_FWD ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+      const uint32_t kb = uint32_t(kt) * BK * Hp * 2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          ra[i] = (kok && 32 * i < arow_lim)
-                      ? *reinterpret_cast<const u32x4*>(a + aoff + uint32_t(32 * i) * H)
-                      : zero4;
-      } else {
-        const uint16_t* a = Ab + int64_t(k0) * H;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          ra[i] = (acol_ok && k0 + kg * 8 + i < KD)
-                      ? *reinterpret_cast<const u32x4*>(a + aoff + uint32_t(i) * H)
-                      : zero4;
+      for (int u = 0; u < NI; ++u) {
+        load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
+        load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
       }
-      const uint16_t* b = Bb + int64_t(k0) * Hp;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rb[i] = (bcol_ok && k0 + kg * 8 + i < KD)
-                    ? *reinterpret_cast<const u32x4*>(b + boff + uint32_t(i) * Hp)
-                    : zero4;
     };
-    // Registers -> LDS buffer `buf`; 8x8 blocks are transposed on the way.
-    // The swizzle of row cg + 32i is that of row cg, and rows 8cg + c share
-    // it in pairs (c, c + 1), so every address is a per-lane base plus a
-    // compile-time offset.
-    const int st_lin = lds_off(cg, kg);                 // forward A rows cg + 32i
-    int st_tr[4];                                       // rows 8cg + c, c = 2p, 2p+1
-#pragma unroll
-    for (int p2 = 0; p2 < 4; ++p2) st_tr[p2] = lds_off(cg * 8 + 2 * p2, kg) - 2 * p2 * (BK * 2);
-    auto store = [&](int buf) {
-      unsigned char* As = lds + buf * 2 * kTileBytes;
-      unsigned char* Bs = As + kTileBytes;
-      if (MODE == MODE_FWD) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<u32x4*>(As + st_lin + i * 32 * (BK * 2)) = ra[i];
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          *reinterpret_cast<u32x4*>(As + st_tr[c >> 1] + c * (BK * 2)) = transpose_col(ra, c);
+    // One k-tile: wait for its stage, then issue the tile 3 ahead into the
+    // stage read one iteration ago, then 32 MFMAs on this stage.
+    auto step = [&](auto S_, int kt) {
+      constexpr int S = decltype(S_)::value;
+      const int after = min(2, nk - 1 - kt);
+      if (after >= 2) wait_vm<4 * NI>();
+      else if (after == 1) wait_vm<2 * NI>();
+      else wait_vm<0>();
+      barrier_lds();
+      if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) % 4>(), kt + 3);
+      unsigned char* As = stage_a<S>();
+      const unsigned char* Bs = stage_b<S>();
+      if (MODE == MODE_FWD && (kt + 1) * BK > H) {
+        // ragged K: the A chunks past H hold the next row's data -- zero them
+        wait_vm<0>();
+        barrier_lds();
+        for (int x = tid; x < kTile / 16; x += kGemmThreads) {
+          const int row = x / CPR, phys = x % CPR;
+          const int kc = phys ^ ((row >> RSH) & (CPR - 1));
+          if (kt * BK + kc * 8 >= H) *reinterpret_cast<u32x4*>(As + x * 16) = u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<u32x4*>(Bs + st_tr[c >> 1] + c * (BK * 2)) = transpose_col(rb, c);
-    };
-    // MFMA operand reads: row wm*128 + 32i + lane%32 (resp. wn) has the
-    // swizzle of lane%32; only the 16-byte chunk 2s + lane/32 varies with s.
-    int rd_a[BK / 16], rd_b[BK / 16];
-#pragma unroll
-    for (int s2 = 0; s2 < BK / 16; ++s2) {
-      rd_a[s2] = lds_off(wm * 128 + (lane & 31), 2 * s2 + (lane >> 5));
-      rd_b[s2] = lds_off(wn * 128 + (lane & 31), 2 * s2 + (lane >> 5));
-    }
-
-    if (nk > 0) {
-      load(0);
-      store(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) load(kt + 1);
-      const unsigned char* As = lds + (kt & 1) * 2 * kTileBytes;
-      const unsigned char* Bs = As + kTileBytes;
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
         bf16x8 af[4], bfr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(As + rd_a[s] + i * 32 * (BK * 2)));
+        for (int i = 0; i < 4; ++i) {
+          if (MODE == MODE_FWD) {
+            af[i] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * 32 * ROWB));
+          } else {
+            const unsigned char* p = As + tr_off[i] + wm * 256 + s * 16 * 512;
+            af[i] = join(lds_tr(p), lds_tr(p + 4 * 512));
+          }
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[j] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Bs + rd_b[s] + j * 32 * (BK * 2)));
+        for (int j = 0; j < 4; ++j) {
+          const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
+          bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (more) store((kt + 1) & 1);
-      __syncthreads();
+    };
+
+    if (0 < nk) issue(std::integral_constant<int, 0>(), 0);
+    if (1 < nk) issue(std::integral_constant<int, 1>(), 1);
+    if (2 < nk) issue(std::integral_constant<int, 2>(), 2);
+    for (int kt = 0; kt < nk; kt += 4) {
+      step(std::integral_constant<int, 0>(), kt);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1>(), kt + 1);
+      if (kt + 2 < nk) step(std::integral_constant<int, 2>(), kt + 2);
+      if (kt + 3 < nk) step(std::integral_constant<int, 3>(), kt + 3);
     }
+    wait_vm<0>();
+    __syncthreads();
 
     // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
     // rows 8*(v/4) + 4*(l/32) + v%4 of its block for v = 0..15.
     if (MODE == MODE_FWD) {
-      // Stage the wave's 128x128 bf16 sub-tile in LDS (rows padded to 272
-      // bytes), then write whole 16-byte row chunks.
-      unsigned char* Cs = lds + wv * (128 * kCRow);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int mm = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const int nn = 32 * j + (lane & 31);
-            *reinterpret_cast<uint16_t*>(Cs + mm * kCRow + nn * 2) =
-                (uint16_t)f32_to_bf16(acc[i][j][v]);
-          }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Per wave, two passes of 64 rows x 128 columns staged as bf16 in the
+      // wave's own 16 KB stage array (256-byte rows), then whole 16-byte row
+      // chunks to global memory.
+      unsigned char* Cs = wv == 0 ? stage_a<0>() : wv == 1 ? stage_a<1>()
+                        : wv == 2 ? stage_a<2>() : stage_a<3>();
       uint16_t* yb = g.y + int64_t(it.row0) * Hp;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        unsigned char* cbase = Cs + 4 * (lane >> 5) * 256 + (lane & 31) * 2;
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16 a = acc[2 * half + i2][j];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int mm = 32 * i2 + 8 * (v >> 2) + (v & 3);
+              *reinterpret_cast<uint16_t*>(cbase + mm * 256 + 64 * j) =
+                  (uint16_t)f32_to_bf16(a[v]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll 4
-      for (int c = lane; c < 128 * 16; c += kWave) {
-        const int rr = c >> 4, cc = c & 15;
-        const int m = wm * 128 + rr;
-        const int n = n0 + wn * 128 + cc * 8;
-        if (m < it.rows && n < Hp)
-          *reinterpret_cast<u32x4*>(yb + uint32_t(m) * Hp + n) =
-              *reinterpret_cast<const u32x4*>(Cs + rr * kCRow + cc * 16);
+        for (int c = lane; c < 64 * 16; c += kWave) {
+          const int rr = c >> 4, cc = c & 15;
+          const int m = wm * 128 + half * 64 + rr;
+          const int n = n0 + wn * 128 + cc * 8;
+          if (m < it.rows && n < Hp)
+            *reinterpret_cast<u32x4*>(yb + uint32_t(m) * Hp + n) =
+                *reinterpret_cast<const u32x4*>(Cs + rr * 256 + cc * 16);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
       __syncthreads();
     } else {
@@ -373,18 +475,16 @@ static size_t gemm_ws_bytes(const moe_cfg* c) {
 static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hipStream_t stream) {
   int rc;
   if (mode == MODE_FWD) {
-    if ((rc = allow_lds(k_gemm<MODE_FWD>, kGemmLds)) != MOE_OK) return rc;
     hipLaunchKernelGGL(k_sched<MODE_FWD>, dim3(1), dim3(1024), 0, stream, s);
   } else {
-    if ((rc = allow_lds(k_gemm<MODE_WGRAD>, kGemmLds)) != MOE_OK) return rc;
     hipLaunchKernelGGL(k_sched<MODE_WGRAD>, dim3(1), dim3(1024), 0, stream, s);
   }
   int G = num_cus();
   G = std::max(8, G - G % 8);
   if (mode == MODE_FWD)
-    hipLaunchKernelGGL(k_gemm<MODE_FWD>, dim3(G), dim3(kGemmThreads), kGemmLds, stream, g);
+    hipLaunchKernelGGL((k_gemm<MODE_FWD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
   else
-    hipLaunchKernelGGL(k_gemm<MODE_WGRAD>, dim3(G), dim3(kGemmThreads), kGemmLds, stream, g);
+    hipLaunchKernelGGL((k_gemm<MODE_WGRAD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
   return hip_status();
 }
 

@@ -213,7 +213,7 @@ def randn_bf16(shape_tuple, seed, device="cpu", chunk_rows=None):
     gen = torch.Generator(device=device)
     for c0 in range(0, rows, chunk_rows):
         c1 = min(rows, c0 + chunk_rows)
-        gen.manual_seed((seed * 65537 + c0) % (2 ** 62))
+        gen.manual_seed((int(seed) * 65537 + c0) % (2 ** 62))
         tmp = torch.randn((c1 - c0,) + tuple(shape_tuple[1:]), generator=gen,
                           device=device, dtype=torch.float32)
         out[c0:c1].copy_(tmp)
