@@ -232,6 +232,9 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time plan/dispatch/gemm/combine "
                     "at every maxvio of the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the R expert-parallel ranks are virtual ranks "
@@ -239,6 +242,13 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     mx.load()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     shape = W.BENCH
     log("routing: zipf maxvio target", args.maxvio)
     ids, gates, s_bias, mv = W.routing_zipf(shape, args.maxvio)

@@ -74,9 +74,15 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 // (wait_vm) before the barrier that publishes it.
 __device__ __forceinline__ void load_lds16(u32x4 rsrc, const unsigned char* lds_dst,
                                            uint32_t voff, uint32_t soff) {
-  const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)lds_dst;
+  // every operand but voff is wave-uniform; make that explicit (scalar regs)
+  const uint32_t l =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds_dst);
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc[q]);
+  const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(l), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+               :: "s"(l), "v"(voff), "s"(r), "s"(so) : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -99,31 +105,48 @@ __device__ __forceinline__ bf16x8 join(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// Pipeline: BK = 32 deep stages, 4 of them.  Each stage's two operand
+// Pipeline: BK = 32 deep stages, kNST of them.  Each stage's two operand
 // tiles are separate LDS arrays so the compiler can tell a read of one stage
 // from the in-flight direct loads of the others and wait only for the
 // stage it reads.
+#ifndef MOONEP_GEMM_STAGES
+#define MOONEP_GEMM_STAGES 4
+#endif
 constexpr int kBK = 32;
-constexpr int kNST = 4;
+constexpr int kNST = MOONEP_GEMM_STAGES;          // 4 x 32 KB of the 160 KB LDS
+static_assert(kNST == 4 || kNST == 5, "stages");
 constexpr int kTile = 256 * kBK * 2;             // 16 KB per operand tile
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa0[kTile], g_sb0[kTile];
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa1[kTile], g_sb1[kTile];
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa2[kTile], g_sb2[kTile];
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa3[kTile], g_sb3[kTile];
+#if MOONEP_GEMM_STAGES == 5
+__shared__ __attribute__((aligned(1024))) unsigned char g_sa4[kTile], g_sb4[kTile];
+#endif
 
 template <int S>
 __device__ __forceinline__ unsigned char* stage_a() {
   if constexpr (S == 0) return g_sa0;
   else if constexpr (S == 1) return g_sa1;
   else if constexpr (S == 2) return g_sa2;
-  else return g_sa3;
+  else if constexpr (S == 3) return g_sa3;
+#if MOONEP_GEMM_STAGES == 5
+  else return g_sa4;
+#else
+  else return nullptr;
+#endif
 }
 template <int S>
 __device__ __forceinline__ unsigned char* stage_b() {
   if constexpr (S == 0) return g_sb0;
   else if constexpr (S == 1) return g_sb1;
   else if constexpr (S == 2) return g_sb2;
-  else return g_sb3;
+  else if constexpr (S == 3) return g_sb3;
+#if MOONEP_GEMM_STAGES == 5
+  else return g_sb4;
+#else
+  else return nullptr;
+#endif
 }
 
 // Workgroup barrier that orders this wave's LDS accesses around it but does
@@ -195,7 +218,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     const WorkItem it = g.items[item];
     const int n0 = tn * BN, m0 = tm * BM;
     const int KD = MODE == MODE_FWD ? H : it.rows;
-    const int nk = (KD + BK - 1) / BK;
+    // k-tiles, rounded up to whole passes over the stages: tiles past the
+    // end load zeros (range-checked loads; ragged forward K is zeroed below)
+    const int nk = ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
 
     // Operand A: forward = xperm rows of the segment (row tile); weight
     // gradient = the same rows read as x^T (col tile over h).
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // Direct loads of k-tile kt into stage S (= kt % 4).
+    // Direct loads of k-tile kt into stage S (= kt % kNST).
     auto issue = [&](auto S_, int kt) {
       constexpr int S = decltype(S_)::value;
       unsigned char* As = stage_a<S>();
@@ -254,20 +279,66 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
       }
     };
-    // One k-tile: wait for its stage, then issue the tile 3 ahead into the
-    // stage read one iteration ago, then 32 MFMAs on this stage.
-    auto step = [&](auto S_, int kt) {
+    // Operand fragments of one 16-deep k substep of stage S.
+    auto read_frags = [&](auto S_, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
       constexpr int S = decltype(S_)::value;
-      const int after = min(2, nk - 1 - kt);
-      if (after >= 2) wait_vm<4 * NI>();
+      const unsigned char* As = stage_a<S>();
+      const unsigned char* Bs = stage_b<S>();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (MODE == MODE_FWD) {
+          af[i] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * 32 * ROWB));
+        } else {
+          const unsigned char* p = As + tr_off[i] + wm * 256 + s * 16 * 512;
+          af[i] = join(lds_tr(p), lds_tr(p + 4 * 512));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
+        bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
+      }
+    };
+    auto mfma16 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // Interleave the 16 MFMAs just issued with the LDS reads of the next
+    // fragments: one read between consecutive MFMAs keeps the matrix pipe fed
+    // while the reads are in flight.
+    auto interleave = [&]() {
+      constexpr int NR = MODE == MODE_FWD ? 12 : 16;
+#pragma unroll
+      for (int x = 0; x < NR; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 - NR, 0);
+    };
+    // Make stage S (k-tile kt) visible to every wave: each wave waits for
+    // its own direct loads of the stage, then the barrier.
+    // At publish(kt) the loads of k-tiles kt+1 .. kt+kNST-2 may stay in flight.
+    auto publish = [&](int kt) {
+      const int after = min(kNST - 2, nk - 1 - kt);
+      if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
+      else if (after >= 2) wait_vm<4 * NI>();
       else if (after == 1) wait_vm<2 * NI>();
       else wait_vm<0>();
       barrier_lds();
-      if (kt + 3 < nk) issue(std::integral_constant<int, (S + 3) % 4>(), kt + 3);
+    };
+    // k-tile kt in stage S.  On entry f0 holds its substep-0 fragments.
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    auto step = [&](auto S_, int kt) {
+      constexpr int S = decltype(S_)::value;
+      constexpr int SN = (S + 1) % kNST;
       unsigned char* As = stage_a<S>();
-      const unsigned char* Bs = stage_b<S>();
       if (MODE == MODE_FWD && (kt + 1) * BK > H) {
-        // ragged K: the A chunks past H hold the next row's data -- zero them
+        // ragged K: the A chunks past H hold the next row's data -- zero
+        // them and re-read this substep's fragments
         wait_vm<0>();
         barrier_lds();
         for (int x = tid; x < kTile / 16; x += kGemmThreads) {
@@ -276,41 +347,45 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
           if (kt * BK + kc * 8 >= H) *reinterpret_cast<u32x4*>(As + x * 16) = u32x4{0, 0, 0, 0};
         }
         __syncthreads();
+        read_frags(S_, 0, fa0, fb0);
       }
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (MODE == MODE_FWD) {
-            af[i] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * 32 * ROWB));
-          } else {
-            const unsigned char* p = As + tr_off[i] + wm * 256 + s * 16 * 512;
-            af[i] = join(lds_tr(p), lds_tr(p + 4 * 512));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
-          bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      // substep 0 MFMAs, substep 1 reads
+      mfma16(fa0, fb0);
+      read_frags(S_, 1, fa1, fb1);
+      interleave();
+      __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+      if (kt + 1 < nk) {
+        // all waves are done with stage S once past this barrier: refill it
+        // with k-tile kt + kNST
+        publish(kt + 1);
+        if (kt + kNST < nk) issue(std::integral_constant<int, S>(), kt + kNST);
       }
+      // substep 1 MFMAs, substep 0 reads of the next stage (stale and unused
+      // after the last k-tile)
+      mfma16(fa1, fb1);
+      read_frags(std::integral_constant<int, SN>(), 0, fa0, fb0);
+      interleave();
     };
 
     if (0 < nk) issue(std::integral_constant<int, 0>(), 0);
     if (1 < nk) issue(std::integral_constant<int, 1>(), 1);
     if (2 < nk) issue(std::integral_constant<int, 2>(), 2);
-    for (int kt = 0; kt < nk; kt += 4) {
+    if (3 < nk) issue(std::integral_constant<int, 3>(), 3);
+    if (kNST == 5 && 4 < nk) issue(std::integral_constant<int, 4 % kNST>(), 4);
+    if (nk > 0) {
+      // k-tile 0: the kNST - 1 later k-tiles (2 NI loads each) may be in flight
+      // (nk is a positive multiple of kNST)
+      if (kNST == 5) wait_vm<8 * NI>();
+      else wait_vm<6 * NI>();
+      barrier_lds();
+      read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
+    }
+    for (int kt = 0; kt < nk; kt += kNST) {
       step(std::integral_constant<int, 0>(), kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1>(), kt + 1);
-      if (kt + 2 < nk) step(std::integral_constant<int, 2>(), kt + 2);
-      if (kt + 3 < nk) step(std::integral_constant<int, 3>(), kt + 3);
+      step(std::integral_constant<int, 1>(), kt + 1);
+      step(std::integral_constant<int, 2>(), kt + 2);
+      step(std::integral_constant<int, 3>(), kt + 3);
+      if (kNST == 5) step(std::integral_constant<int, 4 % kNST>(), kt + 4);
     }
     wait_vm<0>();
     __syncthreads();
@@ -322,7 +397,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // wave's own 16 KB stage array (256-byte rows), then whole 16-byte row
       // chunks to global memory.
       unsigned char* Cs = wv == 0 ? stage_a<0>() : wv == 1 ? stage_a<1>()
-                        : wv == 2 ? stage_a<2>() : stage_a<3>();
+                        : wv == 2 ? stage_a<2>() : stage_a<3>();      // 16 KB each
       uint16_t* yb = g.y + int64_t(it.row0) * Hp;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
