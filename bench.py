@@ -40,6 +40,105 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_bench_shape.txt")
+KERNEL_SOURCES = {"k_gemm<0>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_gemm<1>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_dispatch": "moe_expert_load_amd/csrc/copy.hip",
+                  "k_combine": "moe_expert_load_amd/csrc/copy.hip",
+                  "k_prefetch": "moe_expert_load_amd/csrc/copy.hip",
+                  "k_reduce_grad": "moe_expert_load_amd/csrc/copy.hip",
+                  "k_count": "moe_expert_load_amd/csrc/plan.hip",
+                  "k_plan": "moe_expert_load_amd/csrc/plan.hip",
+                  "k_route": "moe_expert_load_amd/csrc/plan.hip"}
+
+
+def source_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kernel], "moe_expert_load_amd/csrc/common.hpp"):
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel's source changed after the counters were taken."""
+    try:
+        rec = json.loads(open(TRAFFIC_FILE).read().split("\n", 1)[1])
+    except (OSError, ValueError, IndexError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_digest") != source_digest(kernel):
+        return None
+    return k["traffic_bytes"]
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"moonep::(k_\w+)(<\d+>)?", name)
+    if m:
+        # k_gemm<MODE> / k_sched<MODE> keep their mode; other templates are
+        # tuning variants of one kernel
+        keep = m.group(1) in ("k_gemm", "k_sched")
+        return m.group(1) + ((m.group(2) or "") if keep else "")
+    return "copyBuffer" if "copyBuffer" in name else None
+
+
+def summarize_traffic(fetch_csv, write_csv, cmd_fetch, cmd_write):
+    """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs -> TRAFFIC_FILE."""
+    import csv
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            if k:
+                acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        # the calibration copy is the largest copyBuffer dispatch
+        return {k: (max(v) if k == "copyBuffer" else sum(v) / len(v)) for k, v in acc.items()}
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = float(1 << 20)                     # the 1 GiB calibration copy
+    sf, sw = copy_kib / f["copyBuffer"], copy_kib / w["copyBuffer"]
+    out = {"calibration": {"kernel": "__amd_rocclr_copyBuffer (1 GiB device copy)",
+                           "FETCH_SIZE_KiB": f["copyBuffer"], "WRITE_SIZE_KiB": w["copyBuffer"],
+                           "fetch_scale": sf, "write_scale": sw},
+           "commands": [cmd_fetch, cmd_write], "kernels": {}}
+    for k in sorted(set(f) & set(w)):
+        if k == "copyBuffer" or k not in KERNEL_SOURCES:
+            continue
+        out["kernels"][k] = {"FETCH_SIZE_KiB": f[k], "WRITE_SIZE_KiB": w[k],
+                             "read_bytes": f[k] * 1024 * sf, "write_bytes": w[k] * 1024 * sw,
+                             "traffic_bytes": (f[k] * sf + w[k] * sw) * 1024,
+                             "source_digest": source_digest(k)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("# HBM traffic per launch at the bench shape, from rocprofv3 FETCH_SIZE and "
+                 "WRITE_SIZE (KiB per dispatch, averaged), scaled by the same counters on a "
+                 "1 GiB copy; JSON below\n")
+        fh.write(json.dumps(out, indent=1))
+    return out
+
+
+def summarize_stats(stats_csv, cmd, out_md):
+    """rocprofv3 --kernel-trace --stats kernel_stats.csv -> a short markdown table."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel time at the bench shape (rocprofv3 --kernel-trace --stats)", "",
+             "Command (`<repo>` = repository root, `<out>` = output directory): `%s`" % cmd,
+             "", "Summary written by `python bench.py --summarize-stats`.", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        k = _short_kernel(r["Name"])
+        if not k or k == "copyBuffer":
+            continue
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.2f |" % (
+            k, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 class Path:
     """Buffers and calls of one layer at one shape."""
 
@@ -232,10 +331,21 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time plan/dispatch/gemm/combine "
                     "at every maxvio of the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                          "CMD_FETCH", "CMD_WRITE"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "CMD", "OUT_MD"),
+                    help="write a kernel-time summary from rocprofv3 --stats and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size "
                          "reference for hardware byte counters)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic)["calibration"]))
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the R expert-parallel ranks are virtual ranks "
               "inside one GPU's memory; --gpus %d is not supported" % args.gpus)
@@ -278,14 +388,24 @@ def main():
                          "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "ms": ms[name]})
             comps[name + "_GBps"] = ach
     comps["plan_us"] = ms["plan"] * 1e3
+    step_kernel = {"gemm": "k_gemm<0>", "wgrad": "k_gemm<1>", "dispatch": "k_dispatch",
+                   "combine": "k_combine", "prefetch": "k_prefetch",
+                   "reduce_grad": "k_reduce_grad", "plan": None}
+    for r in roof:
+        k = step_kernel[r["step"]]
+        r["traffic"] = measured_traffic(k) if k else None
     dom = max((r for r in roof if r["step"] != "plan"), key=lambda r: r["ms"])
     kernel_of = {"gemm": "k_gemm<0> (grouped GEMM, 256x256 MFMA tiles)",
                  "wgrad": "k_gemm<1> (weight-grad GEMM)",
                  "dispatch": "k_dispatch", "combine": "k_combine",
                  "prefetch": "k_prefetch", "reduce_grad": "k_reduce_grad"}
     gemm_units = units[dom["step"]][1]
+    dom_kernel = {"gemm": "k_gemm<0>", "wgrad": "k_gemm<1>", "dispatch": "k_dispatch",
+                  "combine": "k_combine", "prefetch": "k_prefetch",
+                  "reduce_grad": "k_reduce_grad"}[dom["step"]]
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
-                "unit": dom["unit"], "frac": dom["frac"], "traffic": None,
+                "unit": dom["unit"], "frac": dom["frac"],
+                "traffic": measured_traffic(dom_kernel),
                 "kernel": kernel_of[dom["step"]],
                 "algorithmic_per_launch": gemm_units, "avg_launch_ms": dom["ms"]}
     line = {

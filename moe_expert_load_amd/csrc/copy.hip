@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void k_prefetch(const u32x4* __restrict__ w_ho
 
 // ---------------------------------------------------------------------------
 // dispatch: one wave per token; the row is read once (DU vectors per lane per
-// pass) and written to each of its K destinations.
+// pass) and written to each of its K destinations.  Plain stores: on gfx950
+// they sustain a higher write rate than non-temporal ones for this pattern.
 // ---------------------------------------------------------------------------
 template <int DU>
 __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
 #pragma unroll
       for (int u = 0; u < DU; ++u) {
         const int c = c0 + u * kWave + lane;
-        if (c < hv) __builtin_nontemporal_store(v[u], d + c);
+        if (c < hv) d[c] = v[u];
       }
     }
   }
@@ -75,9 +76,14 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
 
 // ---------------------------------------------------------------------------
 // combine: one wave per token; out = sum_k g_k * y[route_k] in fp32, k
-// ascending, rounded once to bf16.
+// ascending, rounded once to bf16.  The rows of KB routes are loaded before
+// any of them is accumulated, so KB * CU 16-byte loads per lane are in
+// flight.
 // ---------------------------------------------------------------------------
-template <int CU>
+#ifndef MOONEP_COMBINE_KB
+#define MOONEP_COMBINE_KB 8
+#endif
+template <int CU, int KB>
 __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
                                                  const float* __restrict__ gates,
                                                  const int32_t* __restrict__ route,
@@ -94,23 +100,30 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
     for (int u = 0; u < CU; ++u)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int src = __shfl(myroute, k, kWave);
-      const float g = __shfl(mygate, k, kWave);
-      if (src < 0) continue;
-      const u32x4* row = y + int64_t(src) * hv;
-      u32x4 v[CU];
+    for (int k0 = 0; k0 < K; k0 += KB) {
+      u32x4 v[KB][CU];
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
-        const int c = c0 + u * kWave + lane;
-        v[u] = c < hv ? row[c] : u32x4{0, 0, 0, 0};
+      for (int kb = 0; kb < KB; ++kb) {
+        const int src = __shfl(myroute, min(k0 + kb, K - 1), kWave);
+        const bool ok = k0 + kb < K && src >= 0;
+        const u32x4* row = y + int64_t(ok ? src : 0) * hv;
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int c = c0 + u * kWave + lane;
+          // every y row is read exactly once: stream it past the caches
+          v[kb][u] = (ok && c < hv) ? __builtin_nontemporal_load(row + c) : u32x4{0, 0, 0, 0};
+        }
       }
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
+      for (int kb = 0; kb < KB; ++kb) {
+        const float g = k0 + kb < K ? __shfl(mygate, min(k0 + kb, K - 1), kWave) : 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[u][2 * q] = fmaf(g, bf16_lo(v[u][q]), acc[u][2 * q]);
-          acc[u][2 * q + 1] = fmaf(g, bf16_hi(v[u][q]), acc[u][2 * q + 1]);
+        for (int u = 0; u < CU; ++u) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[u][2 * q] = fmaf(g, bf16_lo(v[kb][u][q]), acc[u][2 * q]);
+            acc[u][2 * q + 1] = fmaf(g, bf16_hi(v[kb][u][q]), acc[u][2 * q + 1]);
+          }
         }
       }
     }
@@ -234,9 +247,9 @@ extern "C" int moe_combine(const moe_cfg* cfg, const moe_plan* plan, const moe_b
   const dim3 grid((ntok + 3) / 4), block(256);
   const u32x4* ys = reinterpret_cast<const u32x4*>(y);
   u32x4* od = reinterpret_cast<u32x4*>(out);
-#define MOE_COMBINE(N)                                                                        \
-  hipLaunchKernelGGL(k_combine<N>, grid, block, 0, stream, ys, gates, plan->route, od, ntok, \
-                     cfg->K, hv)
+#define MOE_COMBINE(N)                                                                   \
+  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB>), grid, block, 0, stream, ys, gates, \
+                     plan->route, od, ntok, cfg->K, hv)
   if (cu <= 1) MOE_COMBINE(1);
   else if (cu <= 2) MOE_COMBINE(2);
   else MOE_COMBINE(4);

@@ -16,13 +16,18 @@
 //               go to the 32 workgroups of one XCD (blockIdx % 8 picks the
 //               XCD), so the A panel and the weight panels of neighbouring
 //               tiles are shared in that XCD's L2.
-// Tile: BM = BN = 256, BK = 64; 4 waves in a 2x2 grid, each 128x128 =
-// 4x4 MFMA blocks of 32x32 with fp32 accumulators.  Both operands are
-// staged through LDS (double buffered, 2 x 64 KB) in [row][k] order with a
-// 16-byte-chunk XOR swizzle.  Operands whose k index is strided in memory
-// (the weight [H][H'] in the forward; both operands of the weight
-// gradient) are loaded as 8x8 bf16 blocks and transposed in registers
-// before the LDS store.
+// Tile: BM = BN = 256, BK = 32; 4 waves in a 2x2 grid, each 128x128 =
+// 4x4 MFMA blocks of 32x32 with fp32 accumulators (256 AGPRs per wave).
+// Operands go from global memory straight into LDS (buffer_load ... lds,
+// range-checked so ragged tails read zeros) through a 4-stage ring of
+// separate LDS arrays, with 16-byte-chunk XOR swizzles that make every LDS
+// read conflict free.  An operand whose k index is contiguous (the permuted
+// activations in the forward) is read with ds_read_b128; an operand whose
+// k index is strided (the weight [H][H'], dy, and x^T in the weight
+// gradient) is stored as loaded, [k][col], and read with the transposing
+// ds_read_b64_tr_b16, which returns 4 consecutive k per lane.  Fragment
+// reads of the next 16-deep substep are interleaved with the MFMAs of the
+// current one.
 #include <algorithm>
 #include <type_traits>
 

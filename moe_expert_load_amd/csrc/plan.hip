@@ -44,19 +44,26 @@ __global__ __launch_bounds__(kPlanThreads) void k_count(PlanArgs a) {
   const uint64_t lt = lanemask_lt();
   const int64_t base = int64_t(blockIdx.x) * kRouteWaves * a.L + int64_t(w) * a.L;
   int bad = 0;
-  for (int off = 0; off < a.L; off += kWave) {
-    const int64_t i0 = base + off;
-    if (i0 >= a.N) break;  // uniform across the wave
-    const int64_t i = i0 + lane;
-    int key = E;
-    if (i < a.N) {
-      const int e = a.ids[i];
-      if ((unsigned)e < (unsigned)E) key = e; else bad = 1;
+  const int64_t lim = min<int64_t>(a.N, base + a.L);
+  for (int64_t b0 = base; b0 < lim; b0 += 8 * kWave) {
+    int ids8[8];                                  // 8 rounds of ids in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = b0 + u * kWave + lane;
+      ids8[u] = i < lim ? a.ids[i] : E;
     }
-    const uint64_t act = __ballot(key < E);
-    if (act == 0) continue;
-    const uint64_t m = match_any(key, a.nbits, act);
-    if (key < E && (m & lt) == 0) atomicAdd(&s_cnt[key], (int)__popcll(m));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = b0 + u * kWave + lane;
+      int key = E;
+      if (i < lim) {
+        if ((unsigned)ids8[u] < (unsigned)E) key = ids8[u]; else bad = 1;
+      }
+      const uint64_t act = __ballot(key < E);
+      if (act == 0) continue;
+      const uint64_t m = match_any(key, a.nbits, act);
+      if (key < E && (m & lt) == 0) atomicAdd(&s_cnt[key], (int)__popcll(m));
+    }
   }
   if (bad) s_bad = 1;
   __syncthreads();
@@ -125,44 +132,44 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   if (tid == 0) { sErr = 0; sNm = 0; sNf = 0; }
 
   // 1. Column prefix over chunks: cc[c][e] <- sum of cc[c'][e], c' < c; T_e.
-  int P = 1;
-  if (C > 1 && E <= kPlanThreads / 2) P = min(C, kPlanThreads / E);
-  if (P == 1) {
-    for (int e = tid; e < E; e += kPlanThreads) {
-      int run = 0;
-      int c = 0;
-      for (; c + 8 <= C; c += 8) {
-        int v[8];
+  // C <= kMaxChunks.  Each thread loads its whole share of a column in one
+  // batch (one memory round trip), then writes the exclusive prefixes.
+  {
+    int P = 1;
+    if (C > 1 && E <= kPlanThreads / 2) P = min(C, kPlanThreads / E);
+    if (P == 1) {
+      for (int e = tid; e < E; e += kPlanThreads) {
+        int v[kMaxChunks];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = a.cc[int64_t(c + u) * E + e];
+        for (int u = 0; u < kMaxChunks; ++u) v[u] = u < C ? a.cc[int64_t(u) * E + e] : 0;
+        int run = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) { a.cc[int64_t(c + u) * E + e] = run; run += v[u]; }
+        for (int u = 0; u < kMaxChunks; ++u)
+          if (u < C) { a.cc[int64_t(u) * E + e] = run; run += v[u]; }
+        sT[e] = run;
       }
-      for (; c < C; ++c) {
-        const int v = a.cc[int64_t(c) * E + e];
-        a.cc[int64_t(c) * E + e] = run;
-        run += v;
+    } else {
+      // P >= 2, so a part holds at most kMaxChunks / 2 chunks and P*E <= 1024
+      const bool act = tid < P * E;
+      const int e = tid % E, q = tid / E;
+      const int c0 = q * C / P, c1 = (q + 1) * C / P;
+      int v[kMaxChunks / 2];
+      int sum = 0;
+#pragma unroll
+      for (int u = 0; u < kMaxChunks / 2; ++u) {
+        v[u] = (act && c0 + u < c1) ? a.cc[int64_t(c0 + u) * E + e] : 0;
+        sum += v[u];
       }
-      sT[e] = run;
-    }
-  } else {
-    const bool act = tid < P * E;
-    const int e = tid % E, q = tid / E;
-    const int c0 = q * C / P, c1 = (q + 1) * C / P;
-    int sum = 0;
-    if (act)
-      for (int c = c0; c < c1; ++c) sum += a.cc[int64_t(c) * E + e];
-    if (act) sScan[tid] = sum;
-    __syncthreads();
-    if (act) {
-      int run = 0;
-      for (int q2 = 0; q2 < q; ++q2) run += sScan[q2 * E + e];
-      for (int c = c0; c < c1; ++c) {
-        const int v = a.cc[int64_t(c) * E + e];
-        a.cc[int64_t(c) * E + e] = run;
-        run += v;
+      if (act) sScan[tid] = sum;
+      __syncthreads();
+      if (act) {
+        int run = 0;
+        for (int q2 = 0; q2 < q; ++q2) run += sScan[q2 * E + e];
+#pragma unroll
+        for (int u = 0; u < kMaxChunks / 2; ++u)
+          if (c0 + u < c1) { a.cc[int64_t(c0 + u) * E + e] = run; run += v[u]; }
+        if (q == P - 1) sT[e] = run;
       }
-      if (q == P - 1) sT[e] = run;
     }
   }
   __syncthreads();
@@ -440,20 +447,34 @@ __global__ __launch_bounds__(kPlanThreads) void k_route(PlanArgs a) {
     return;
   }
   int* cnt = s_cnt + w * E;
+  int* s_taken = s_cnt + kRouteWaves * E;     // [E] LDS copies of the
+  int* s_home = s_taken + E;                  // [E] per-expert route tables
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_taken[e] = a.taken[e];
+    s_home[e] = a.home_base[e];
+  }
   for (int e = lane; e < E; e += kWave) cnt[e] = 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // pass A: per-wave counts
-  for (int64_t i0 = base; i0 < lim; i0 += kWave) {
-    const int64_t i = i0 + lane;
-    const int key = i < lim ? a.ids[i] : E;
-    const uint64_t act = __ballot(key < E);
-    const uint64_t m = match_any(key, a.nbits, act);
-    if (key < E && (m & lt) == 0) cnt[key] += (int)__popcll(m);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int64_t b0 = base; b0 < lim; b0 += 8 * kWave) {
+    int ids8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = b0 + u * kWave + lane;
+      ids8[u] = i < lim ? a.ids[i] : E;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int key = ids8[u];
+      const uint64_t act = __ballot(key < E);
+      const uint64_t m = match_any(key, a.nbits, act);
+      if (key < E && (m & lt) == 0) cnt[key] += (int)__popcll(m);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   }
   __syncthreads();
   // exclusive prefix over the 16 waves, on top of the chunk's prefix
@@ -468,16 +489,24 @@ __global__ __launch_bounds__(kPlanThreads) void k_route(PlanArgs a) {
   }
   __syncthreads();
   // pass B: ranks and destinations
-  for (int64_t i0 = base; i0 < lim; i0 += kWave) {
-    const int64_t i = i0 + lane;
-    const int key = i < lim ? a.ids[i] : E;
+  for (int64_t b0 = base; b0 < lim; b0 += 8 * kWave) {
+   int ids8[8];
+#pragma unroll
+   for (int u = 0; u < 8; ++u) {
+     const int64_t i = b0 + u * kWave + lane;
+     ids8[u] = i < lim ? a.ids[i] : E;
+   }
+#pragma unroll
+   for (int u = 0; u < 8; ++u) {
+    const int64_t i = b0 + u * kWave + lane;
+    const int key = ids8[u];
     const uint64_t act = __ballot(key < E);
     const uint64_t m = match_any(key, a.nbits, act);
     if (key < E) {
       const int p = cnt[key] + (int)__popcll(m & lt);
       int dest = -1;
-      if (p >= a.taken[key]) {
-        dest = a.home_base[key] + p;
+      if (p >= s_taken[key]) {
+        dest = s_home[key] + p;
       } else {
         const int q0 = a.mptr[key], q1 = q0 + a.mcnt[key];
         for (int q = q0; q < q1; ++q)
@@ -492,6 +521,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_route(PlanArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+   }
   }
 }
 
@@ -549,7 +579,7 @@ extern "C" int moe_plan_run(const moe_cfg* cfg, const int32_t* topk_ids, const m
 
   const size_t lds_count = sizeof(int) * cfg->E;
   const size_t lds_plan = plan_lds_bytes(cfg, L);
-  const size_t lds_route = sizeof(int) * size_t(kRouteWaves) * cfg->E;
+  const size_t lds_route = sizeof(int) * size_t(kRouteWaves + 2) * cfg->E;
   if ((rc = allow_lds(k_plan, lds_plan)) != MOE_OK) return rc;
   if ((rc = allow_lds(k_route, lds_route)) != MOE_OK) return rc;
   if (L.C > 0) hipLaunchKernelGGL(k_count, dim3(L.C), dim3(kPlanThreads), lds_count, stream, a);
