@@ -39,21 +39,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// Cross-lane reductions with DPP (no LDS round trip).  row_shr:1,2,4,8 scan
+// each row of 16 lanes; row_bcast:15 then row_bcast:31 carry the row totals
+// into the later rows.  Every lane of the wave must be active.
+#define MOONEP_DPP(old, v, ctrl, rows) __builtin_amdgcn_update_dpp((old), (v), (ctrl), (rows), 0xf, false)
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int t = __shfl_up(v, d, kWave);
-    if (lane >= d) v += t;
-  }
+  v += MOONEP_DPP(0, v, 0x111, 0xf);
+  v += MOONEP_DPP(0, v, 0x112, 0xf);
+  v += MOONEP_DPP(0, v, 0x114, 0xf);
+  v += MOONEP_DPP(0, v, 0x118, 0xf);
+  v += MOONEP_DPP(0, v, 0x142, 0xa);
+  v += MOONEP_DPP(0, v, 0x143, 0xc);
   return v;
 }
 
+// Value of lane `src` (uniform) in every lane.
+__device__ __forceinline__ int wave_bcast(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  return wave_bcast(wave_incl_scan(v), kWave - 1);
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+  v = max(v, MOONEP_DPP(v, v, 0x111, 0xf));
+  v = max(v, MOONEP_DPP(v, v, 0x112, 0xf));
+  v = max(v, MOONEP_DPP(v, v, 0x114, 0xf));
+  v = max(v, MOONEP_DPP(v, v, 0x118, 0xf));
+  v = max(v, MOONEP_DPP(v, v, 0x142, 0xa));
+  v = max(v, MOONEP_DPP(v, v, 0x143, 0xc));
+  return wave_bcast(v, kWave - 1);
 }
 
 // Lanes of the wave whose key equals this lane's key, restricted to `active`.

@@ -143,9 +143,10 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
 
 // ---------------------------------------------------------------------------
 // reduce_grad: grid (chunks, E); y-block i handles the i-th expert that has
-// consumers.  Its consumers are the CSR entries of its moves, already in
-// ascending receiver rank; entries with b >= B (inference overflow) own no
-// slot and are skipped.
+// consumers.  Its consumers are the CSR entries of its moves (fill order);
+// each receiver holds at most one of them, so they are placed by receiver
+// rank and compacted, and the sum runs over ascending ranks.  Entries with
+// b >= B (inference overflow) own no slot and are skipped.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_reduce_grad(f32x4* __restrict__ grad_home,
                                                      f32x4* __restrict__ grad_pref,
@@ -154,20 +155,32 @@ __global__ __launch_bounds__(256) void k_reduce_grad(f32x4* __restrict__ grad_ho
                                                      const int32_t* __restrict__ mptr,
                                                      const int32_t* __restrict__ mcnt,
                                                      const int32_t* __restrict__ cs_dst,
-                                                     const int32_t* __restrict__ cs_b, int B,
-                                                     int64_t nvec) {
+                                                     const int32_t* __restrict__ cs_b, int R,
+                                                     int B, int64_t nvec) {
+  __shared__ int s_rank[MOE_MAX_R];
   __shared__ int s_slot[MOE_MAX_R];
   __shared__ int s_n;
   if ((int)blockIdx.y >= misc[0]) return;
   const int e = cons[blockIdx.y];
-  if (threadIdx.x == 0) {
+  for (int r = threadIdx.x; r < R; r += blockDim.x) s_rank[r] = -1;
+  __syncthreads();
+  const int q0 = mptr[e], q1 = q0 + mcnt[e];
+  for (int q = q0 + (int)threadIdx.x; q < q1; q += blockDim.x) {
+    const int b = cs_b[q], d = cs_dst[q];
+    if (b < B && (unsigned)d < (unsigned)R) s_rank[d] = d * B + b;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = lane_id();
+    const uint64_t lt = lanemask_lt();
     int k = 0;
-    const int q0 = mptr[e], q1 = q0 + mcnt[e];
-    for (int q = q0; q < q1; ++q) {
-      const int b = cs_b[q];
-      if (b < B && k < MOE_MAX_R) s_slot[k++] = cs_dst[q] * B + b;
+    for (int r0 = 0; r0 < R; r0 += kWave) {
+      const int v = r0 + lane < R ? s_rank[r0 + lane] : -1;
+      const uint64_t bal = __ballot(v >= 0);
+      if (v >= 0) s_slot[k + (int)__popcll(bal & lt)] = v;
+      k += (int)__popcll(bal);
     }
-    s_n = k;
+    if (lane == 0) s_n = k;
   }
   __syncthreads();
   const int ns = s_n;
@@ -274,6 +287,6 @@ extern "C" int moe_reduce_grad(const moe_cfg* cfg, const moe_plan* plan, float* 
                      reinterpret_cast<f32x4*>(grad_home), reinterpret_cast<f32x4*>(grad_pref),
                      ws_i32(ws, L.off_cons), ws_i32(ws, L.off_misc), ws_i32(ws, L.off_mptr),
                      ws_i32(ws, L.off_mcnt), ws_i32(ws, L.off_cs_dst), ws_i32(ws, L.off_cs_b),
-                     cfg->B, nvec);
+                     cfg->R, cfg->B, nvec);
   return hip_status();
 }

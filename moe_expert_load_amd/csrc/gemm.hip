@@ -110,21 +110,29 @@ __device__ __forceinline__ bf16x8 join(u32x2 lo, u32x2 hi) {
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// Pipeline: BK = 32 deep stages, kNST of them.  Each stage's two operand
-// tiles are separate LDS arrays so the compiler can tell a read of one stage
-// from the in-flight direct loads of the others and wait only for the
-// stage it reads.
-#ifndef MOONEP_GEMM_STAGES
+// Pipeline: kNST stages of BK-deep k-tiles.  BK = 64 (2 stages of 64 KB)
+// makes every row of the k-contiguous forward operand a whole 128-byte line
+// per stage; BK = 32 (4 stages of 32 KB) keeps more stages in flight.  Each
+// stage's two operand tiles are separate LDS arrays so the compiler can
+// tell a read of one stage from the in-flight direct loads of the others.
+#ifndef MOONEP_GEMM_BK
+#define MOONEP_GEMM_BK 32
+#endif
+#if MOONEP_GEMM_BK == 64
+#define MOONEP_GEMM_STAGES 2
+#elif !defined(MOONEP_GEMM_STAGES)
 #define MOONEP_GEMM_STAGES 4
 #endif
-constexpr int kBK = 32;
-constexpr int kNST = MOONEP_GEMM_STAGES;          // 4 x 32 KB of the 160 KB LDS
-static_assert(kNST == 4 || kNST == 5, "stages");
-constexpr int kTile = 256 * kBK * 2;             // 16 KB per operand tile
+constexpr int kBK = MOONEP_GEMM_BK;
+constexpr int kNST = MOONEP_GEMM_STAGES;
+static_assert((kBK == 64 && kNST == 2) || (kBK == 32 && (kNST == 4 || kNST == 5)), "pipeline");
+constexpr int kTile = 256 * kBK * 2;             // bytes per operand tile
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa0[kTile], g_sb0[kTile];
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa1[kTile], g_sb1[kTile];
+#if MOONEP_GEMM_STAGES >= 4
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa2[kTile], g_sb2[kTile];
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa3[kTile], g_sb3[kTile];
+#endif
 #if MOONEP_GEMM_STAGES == 5
 __shared__ __attribute__((aligned(1024))) unsigned char g_sa4[kTile], g_sb4[kTile];
 #endif
@@ -133,24 +141,35 @@ template <int S>
 __device__ __forceinline__ unsigned char* stage_a() {
   if constexpr (S == 0) return g_sa0;
   else if constexpr (S == 1) return g_sa1;
+#if MOONEP_GEMM_STAGES >= 4
   else if constexpr (S == 2) return g_sa2;
   else if constexpr (S == 3) return g_sa3;
-#if MOONEP_GEMM_STAGES == 5
-  else return g_sa4;
-#else
-  else return nullptr;
 #endif
+#if MOONEP_GEMM_STAGES == 5
+  else if constexpr (S == 4) return g_sa4;
+#endif
+  else return nullptr;
 }
 template <int S>
 __device__ __forceinline__ unsigned char* stage_b() {
   if constexpr (S == 0) return g_sb0;
   else if constexpr (S == 1) return g_sb1;
+#if MOONEP_GEMM_STAGES >= 4
   else if constexpr (S == 2) return g_sb2;
   else if constexpr (S == 3) return g_sb3;
+#endif
 #if MOONEP_GEMM_STAGES == 5
-  else return g_sb4;
-#else
+  else if constexpr (S == 4) return g_sb4;
+#endif
   else return nullptr;
+}
+
+// Per-wave 16 KB staging area of the forward epilogue (reuses stage tiles).
+__device__ __forceinline__ unsigned char* epilogue_area(int wv) {
+#if MOONEP_GEMM_STAGES >= 4
+  return wv == 0 ? g_sa0 : wv == 1 ? g_sa1 : wv == 2 ? g_sa2 : g_sa3;
+#else
+  return wv == 0 ? g_sa0 : wv == 1 ? g_sb0 : wv == 2 ? g_sa1 : g_sb1;
 #endif
 }
 
@@ -160,10 +179,11 @@ __device__ __forceinline__ unsigned char* stage_b() {
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
 // Tiles of one pipeline stage:
-//  * "row tile" [256 rows][32 k] (forward A, k contiguous): 16-byte chunk kc
-//    of row m is stored at chunk kc ^ ((m >> 2) & 3), so 16 consecutive rows
+//  * "row tile" [256 rows][BK k] (forward A, k contiguous): 16-byte chunk kc
+//    of row m is stored at chunk kc ^ ((m >> RSH) & (CPR - 1)) (CPR = BK/8
+//    chunks per row, 2^RSH rows per 256 bytes), so 16 consecutive rows
 //    reading one chunk hit 64 distinct banks;
-//  * "col tile" [32 k][256 cols] (weights, dy, and x^T in the weight
+//  * "col tile" [BK k][256 cols] (weights, dy, and x^T in the weight
 //    gradient; columns contiguous): chunk c of row k is stored at
 //    c ^ (4 * (k % 4)), so a transposing read of 4 rows x 4 chunks per 32
 //    lanes is conflict free.
@@ -174,7 +194,7 @@ struct GemmTile {
   static constexpr int BK = kBK;
   static constexpr int ROWB = BK * 2;          // bytes per row-tile row
   static constexpr int CPR = BK / 8;           // 16-byte chunks per row-tile row
-  static constexpr int RSH = 2;                // rows per 256 bytes = 1 << RSH
+  static constexpr int RSH = CPR == 8 ? 1 : 2;  // rows per 256 bytes = 1 << RSH
   static constexpr int NI = kTile / 1024 / 4;  // 1 KB loads per wave per operand
   static constexpr int RPI = 1024 / ROWB;      // row-tile rows per load
 };
@@ -183,7 +203,8 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   using T = GemmTile<MODE>;
   constexpr int BK = T::BK, ROWB = T::ROWB, CPR = T::CPR, RSH = T::RSH, NI = T::NI;
-  static_assert(NI == 4 && CPR == 4, "tile geometry");
+  static_assert(NI * 4096 == kTile && (CPR == 4 || CPR == 8), "tile geometry");
+  constexpr int SUB = BK / 16;                 // MFMA k substeps per stage
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -330,8 +351,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     auto publish = [&](int kt) {
       const int after = min(kNST - 2, nk - 1 - kt);
       if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
-      else if (after >= 2) wait_vm<4 * NI>();
-      else if (after == 1) wait_vm<2 * NI>();
+      else if (kNST >= 4 && after >= 2) wait_vm<4 * NI>();
+      else if (kNST >= 3 && after == 1) wait_vm<2 * NI>();
       else wait_vm<0>();
       barrier_lds();
     };
@@ -354,10 +375,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         __syncthreads();
         read_frags(S_, 0, fa0, fb0);
       }
-      // substep 0 MFMAs, substep 1 reads
+      // substeps 0 .. SUB-2: MFMAs on one fragment set while the next
+      // substep's fragments are read into the other
       mfma16(fa0, fb0);
       read_frags(S_, 1, fa1, fb1);
       interleave();
+      if constexpr (SUB == 4) {
+        mfma16(fa1, fb1);
+        read_frags(S_, 2, fa0, fb0);
+        interleave();
+        mfma16(fa0, fb0);
+        read_frags(S_, 3, fa1, fb1);
+        interleave();
+      }
       __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
       if (kt + 1 < nk) {
         // all waves are done with stage S once past this barrier: refill it
@@ -365,32 +395,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         publish(kt + 1);
         if (kt + kNST < nk) issue(std::integral_constant<int, S>(), kt + kNST);
       }
-      // substep 1 MFMAs, substep 0 reads of the next stage (stale and unused
-      // after the last k-tile)
+      // last substep's MFMAs, substep 0 reads of the next stage (stale and
+      // unused after the last k-tile)
       mfma16(fa1, fb1);
       read_frags(std::integral_constant<int, SN>(), 0, fa0, fb0);
       interleave();
     };
 
-    if (0 < nk) issue(std::integral_constant<int, 0>(), 0);
-    if (1 < nk) issue(std::integral_constant<int, 1>(), 1);
-    if (2 < nk) issue(std::integral_constant<int, 2>(), 2);
-    if (3 < nk) issue(std::integral_constant<int, 3>(), 3);
-    if (kNST == 5 && 4 < nk) issue(std::integral_constant<int, 4 % kNST>(), 4);
-    if (nk > 0) {
-      // k-tile 0: the kNST - 1 later k-tiles (2 NI loads each) may be in flight
-      // (nk is a positive multiple of kNST)
-      if (kNST == 5) wait_vm<8 * NI>();
-      else wait_vm<6 * NI>();
-      barrier_lds();
-      read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
+    if (nk > 0) {                                               // then nk >= kNST
+    issue(std::integral_constant<int, 0>(), 0);
+    issue(std::integral_constant<int, 1>(), 1);
+    if constexpr (kNST >= 4) {
+      issue(std::integral_constant<int, 2 % kNST>(), 2);
+      issue(std::integral_constant<int, 3 % kNST>(), 3);
     }
+    if constexpr (kNST == 5) issue(std::integral_constant<int, 4 % kNST>(), 4);
+    // k-tile 0 has landed once the kNST - 1 later k-tiles (2 NI loads each)
+    // are all that is left in flight
+    wait_vm<(kNST - 1) * 2 * NI>();
+    barrier_lds();
+    read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
     for (int kt = 0; kt < nk; kt += kNST) {
       step(std::integral_constant<int, 0>(), kt);
       step(std::integral_constant<int, 1>(), kt + 1);
-      step(std::integral_constant<int, 2>(), kt + 2);
-      step(std::integral_constant<int, 3>(), kt + 3);
-      if (kNST == 5) step(std::integral_constant<int, 4 % kNST>(), kt + 4);
+      if constexpr (kNST >= 4) {
+        step(std::integral_constant<int, 2 % kNST>(), kt + 2);
+        step(std::integral_constant<int, 3 % kNST>(), kt + 3);
+      }
+      if constexpr (kNST == 5) step(std::integral_constant<int, 4 % kNST>(), kt + 4);
+    }
     }
     wait_vm<0>();
     __syncthreads();
@@ -401,8 +434,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // Per wave, two passes of 64 rows x 128 columns staged as bf16 in the
       // wave's own 16 KB stage array (256-byte rows), then whole 16-byte row
       // chunks to global memory.
-      unsigned char* Cs = wv == 0 ? stage_a<0>() : wv == 1 ? stage_a<1>()
-                        : wv == 2 ? stage_a<2>() : stage_a<3>();      // 16 KB each
+      unsigned char* Cs = epilogue_area(wv);
       uint16_t* yb = g.y + int64_t(it.row0) * Hp;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {

@@ -37,11 +37,16 @@ struct PlanLayout {
   int M;          // move capacity E + R - 1
   int nbits;      // bits needed for keys in [0, E]
   size_t off_cc, off_badc, off_taken, off_home_base, off_mptr, off_mcnt, off_cs_lo, off_cs_hi,
-      off_cs_base, off_cs_dst, off_cs_b, off_cons, off_misc, bytes;
+      off_cs_base, off_cs_dst, off_cs_b, off_cons, off_hpre, off_spre, off_rinfo, off_ocum,
+      off_misc, bytes;
 };
 
 constexpr int kRouteWaves = 16;
-constexpr int kMaxChunks = 64;
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+#ifndef MOONEP_PLAN_CHUNKS
+#define MOONEP_PLAN_CHUNKS 256
+#endif
+constexpr int kMaxChunks = MOONEP_PLAN_CHUNKS;
 
 inline PlanLayout plan_layout(const moe_cfg* c) {
   PlanLayout p{};
@@ -68,6 +73,10 @@ inline PlanLayout plan_layout(const moe_cfg* c) {
   p.off_cs_dst = take(p.M);
   p.off_cs_b = take(p.M);
   p.off_cons = take(c->E);
+  p.off_hpre = take(size_t(c->E) + c->R);                 // R * (E/R + 1)
+  p.off_spre = take(size_t(c->R) * (c->B + 1));
+  p.off_rinfo = take(size_t(3) * c->R);
+  p.off_ocum = take(p.M);
   p.off_misc = take(64);
   p.bytes = o;
   return p;
@@ -90,6 +99,7 @@ inline int hip_status() {
 // Raises a kernel's dynamic LDS limit once (needed above 64 KB on gfx950).
 template <typename F>
 inline int allow_lds(F* kernel, size_t bytes) {
+  if (bytes > kMaxLds) return MOE_ELIMIT;
   if (bytes <= 65536) return MOE_OK;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);

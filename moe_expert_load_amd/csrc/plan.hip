@@ -6,12 +6,13 @@
 // every token's destination); "MoonEP : l'équilibrage parfait", Le théorème
 // (lemma: a receiver's remote slots come from a single rank).
 //
-// Three launches, all sized from the configuration only:
-//   k_count  C workgroups x 16 waves: per-chunk expert counts (ballot match)
-//   k_plan   1 workgroup: column prefix of the chunk counts, T_e, loads, the
-//            fills (wave 0), cu_seqlens per rank, per-expert route tables
-//   k_route  C workgroups x 16 waves: stable rank of each slot inside its
-//            expert, then its destination row
+// Four launches, all sized from the configuration only:
+//   k_count   C workgroups x 16 waves: per-chunk expert counts (LDS atomics)
+//   k_colscan E/64 workgroups: prefix of the chunk counts over chunks, T_e
+//   k_plan    1 workgroup: loads, the fills (wave 0), cu_seqlens per rank,
+//             per-expert route tables
+//   k_route   C workgroups x 16 waves: stable rank of each slot inside its
+//             expert, then its destination row
 #include "common.hpp"
 #include "host.hpp"
 
@@ -19,19 +20,23 @@ namespace moonep {
 
 constexpr int kPlanThreads = kRouteWaves * kWave;  // 1024
 
+template <int N>
+struct IntTag {
+  static constexpr int value = N;
+};
+
 struct PlanArgs {
   const int32_t* ids;
   int32_t N, R, S, E, K, B, mode, n, SK, L, C, M, nbits;
   int32_t *counts, *load0, *route, *cu, *slot_expert, *n_red, *src_rank, *moves, *status;
   int32_t *cc, *badc, *taken, *home_base, *mptr, *mcnt, *cs_lo, *cs_hi, *cs_base, *cs_dst, *cs_b,
-      *cons, *misc;
+      *cons, *hpre, *spre, *rinfo, *ocum, *misc;
 };
 
 // ---------------------------------------------------------------------------
 // k_count: chunk c covers slots [c*16L, (c+1)*16L); wave w of it the L slots
-// starting at c*16L + w*L.  Within a wave, lanes naming the same expert are
-// grouped with a ballot per key bit and only the lowest such lane adds the
-// group size, so LDS atomics are one per distinct expert per 64 slots.
+// starting at c*16L + w*L.  Every valid slot adds one to its expert's LDS
+// counter (the LDS atomic unit serialises lanes that share an address).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void k_count(PlanArgs a) {
   extern __shared__ int s_cnt[];
@@ -41,7 +46,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_count(PlanArgs a) {
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  const uint64_t lt = lanemask_lt();
   const int64_t base = int64_t(blockIdx.x) * kRouteWaves * a.L + int64_t(w) * a.L;
   int bad = 0;
   const int64_t lim = min<int64_t>(a.N, base + a.L);
@@ -55,14 +59,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_count(PlanArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t i = b0 + u * kWave + lane;
-      int key = E;
       if (i < lim) {
-        if ((unsigned)ids8[u] < (unsigned)E) key = ids8[u]; else bad = 1;
+        if ((unsigned)ids8[u] < (unsigned)E) atomicAdd(&s_cnt[ids8[u]], 1); else bad = 1;
       }
-      const uint64_t act = __ballot(key < E);
-      if (act == 0) continue;
-      const uint64_t m = match_any(key, a.nbits, act);
-      if (key < E && (m & lt) == 0) atomicAdd(&s_cnt[key], (int)__popcll(m));
     }
   }
   if (bad) s_bad = 1;
@@ -102,6 +101,46 @@ __device__ int block_excl_scan(int* arr, int n, int* scratch) {
 }
 
 // ---------------------------------------------------------------------------
+// k_colscan: cc[c][e] <- sum of cc[c'][e] over c' < c, and T_e (the counts
+// output).  A workgroup takes 64 experts; its 16 waves split the C chunks.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void k_colscan(PlanArgs a) {
+  constexpr int kPer = kMaxChunks / kRouteWaves;
+  __shared__ int s_part[kRouteWaves][kWave];
+  const int E = a.E, C = a.C;
+  const int lane = lane_id(), g = threadIdx.x / kWave;
+  const int e = blockIdx.x * kWave + lane;
+  const int cpg = (C + kRouteWaves - 1) / kRouteWaves;     // <= kPer
+  const int c0 = g * cpg;
+  int v[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = c0 + u;
+    v[u] = (e < E && u < cpg && c < C) ? a.cc[int64_t(c) * E + e] : 0;
+    sum += v[u];
+  }
+  s_part[g][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q = 0; q < g; ++q) run += s_part[q][lane];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = c0 + u;
+    if (e < E && u < cpg && c < C) {
+      a.cc[int64_t(c) * E + e] = run;
+      run += v[u];
+    }
+  }
+  if (g == kRouteWaves - 1 && e < E) a.counts[e] = run;   // groups 0..15 cover all chunks
+}
+
+// No slots at all (S == 0): T_e = 0.
+__global__ __launch_bounds__(kPlanThreads) void k_zero_counts(PlanArgs a) {
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.counts[e] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // k_plan: one workgroup of 1024 threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
@@ -112,66 +151,27 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   int* sTaken = sT + E;         // [E] slots of e moved away from home
   int* sMcnt = sTaken + E;      // [E] moves of e
   int* sMptr = sMcnt + E;       // [E] CSR start of e's moves
-  int* sRun = sMptr + E;        // [E] scratch
-  int* sLoad = sRun + E;        // [R] current load
-  int* sLoad0 = sLoad + R;      // [R] initial load
-  int* sCursor = sLoad0 + R;    // [R] next home expert a donor gives
-  int* sRecv = sCursor + R;     // [R] fill index that filled rank r, or -1
-  int* sFu = sRecv + R;         // [R] fill -> receiver
-  int* sFo = sFu + R;           // [R] fill -> donor
+  int* sLoad0 = sMptr + E;      // [R] initial load
+  int* sRecv = sLoad0 + R;      // [R] fill index that filled rank r, or -1
+  int* sFo = sRecv + R;         // [R] fill -> donor
   int* sFm0 = sFo + R;          // [R] fill -> first move
   int* sFm1 = sFm0 + R;         // [R] fill -> end move
   int* sMe = sFm1 + R;          // [M] move -> expert
   int* sMu = sMe + M;           // [M] move -> receiver
   int* sMlo = sMu + M;          // [M] move -> first in-expert rank
   int* sMhi = sMlo + M;         // [M] move -> end in-expert rank
-  int* sMpos = sMhi + M;        // [M] move -> CSR position
-  int* sScan = sMpos + M;       // [1024 + 32]
+  int* sMpos = sMhi + M;        // [M] move -> index among its expert's moves
+  int* sHpre = sMpos + M;       // [R*(n+1)] per rank: prefix of home row lengths
+  int* sSpre = sHpre + R * (n + 1);  // [R*(B+1)] per rank: prefix of prefetch rows
+  int* sOcum = sSpre + R * (B + 1);  // [M] inclusive prefix over overflow moves
+  int* sOt = sLoad0;            // [R] overflow rows per rank (after the fills)
+  int* sScan = sOcum + M;       // [1024 + 32]
   __shared__ int sErr, sNm, sNf;
 
   if (tid == 0) { sErr = 0; sNm = 0; sNf = 0; }
 
-  // 1. Column prefix over chunks: cc[c][e] <- sum of cc[c'][e], c' < c; T_e.
-  // C <= kMaxChunks.  Each thread loads its whole share of a column in one
-  // batch (one memory round trip), then writes the exclusive prefixes.
-  {
-    int P = 1;
-    if (C > 1 && E <= kPlanThreads / 2) P = min(C, kPlanThreads / E);
-    if (P == 1) {
-      for (int e = tid; e < E; e += kPlanThreads) {
-        int v[kMaxChunks];
-#pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u) v[u] = u < C ? a.cc[int64_t(u) * E + e] : 0;
-        int run = 0;
-#pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u)
-          if (u < C) { a.cc[int64_t(u) * E + e] = run; run += v[u]; }
-        sT[e] = run;
-      }
-    } else {
-      // P >= 2, so a part holds at most kMaxChunks / 2 chunks and P*E <= 1024
-      const bool act = tid < P * E;
-      const int e = tid % E, q = tid / E;
-      const int c0 = q * C / P, c1 = (q + 1) * C / P;
-      int v[kMaxChunks / 2];
-      int sum = 0;
-#pragma unroll
-      for (int u = 0; u < kMaxChunks / 2; ++u) {
-        v[u] = (act && c0 + u < c1) ? a.cc[int64_t(c0 + u) * E + e] : 0;
-        sum += v[u];
-      }
-      if (act) sScan[tid] = sum;
-      __syncthreads();
-      if (act) {
-        int run = 0;
-        for (int q2 = 0; q2 < q; ++q2) run += sScan[q2 * E + e];
-#pragma unroll
-        for (int u = 0; u < kMaxChunks / 2; ++u)
-          if (c0 + u < c1) { a.cc[int64_t(c0 + u) * E + e] = run; run += v[u]; }
-        if (q == P - 1) sT[e] = run;
-      }
-    }
-  }
+  // 1. T_e from k_colscan.
+  for (int e = tid; e < E; e += kPlanThreads) sT[e] = a.counts[e];
   __syncthreads();
 
   // 2. Loads and validity.
@@ -183,13 +183,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     for (int r = tid; r < R; r += kPlanThreads) {
       int s = 0;
       for (int j = 0; j < n; ++j) s += sT[r * n + j];
-      sLoad[r] = s;
       sLoad0[r] = s;
+      a.load0[r] = s;
       sRecv[r] = -1;
-      sCursor[r] = r * n;
       tot += s;
     }
-    for (int e = tid; e < E; e += kPlanThreads) { sTaken[e] = 0; sMcnt[e] = 0; sRun[e] = 0; }
+    for (int e = tid; e < E; e += kPlanThreads) { sTaken[e] = 0; sMcnt[e] = 0; }
     // total load must be R*S*K (it is unless ids were out of range)
     int t32 = (int)tot;  // R*S*K < 2^31
     t32 = wave_sum(t32);
@@ -203,8 +202,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     __syncthreads();
   }
 
-  if (sErr & (MOE_STATUS_BAD_ID | MOE_STATUS_UNBALANCED)) {
-    // No plan: leave every rank empty; k_route writes route = -1.
+  // No plan: every rank empty, no moves; k_route writes route = -1.
+  auto no_plan = [&]() {
     for (int e = tid; e < E; e += kPlanThreads) { a.counts[e] = sT[e]; a.mcnt[e] = 0; }
     for (int r = tid; r < R; r += kPlanThreads) {
       a.load0[r] = sLoad0[r];
@@ -217,190 +216,268 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       a.status[0] = 0; a.status[1] = 0; a.status[2] = sErr; a.status[3] = 0;
       a.misc[0] = 0;
     }
+  };
+  if (sErr & (MOE_STATUS_BAD_ID | MOE_STATUS_UNBALANCED)) {
+    no_plan();
     return;
   }
 
   // 3. The fills, on wave 0 (sequential by construction: at most R-1).
-  if (wave == 0) {
-    volatile int* vLoad = sLoad;
-    volatile int* vT = sT;
-    volatile int* vTaken = sTaken;
-    volatile int* vMcnt = sMcnt;
-    volatile int* vCursor = sCursor;
-    volatile int* vRecv = sRecv;
-    volatile int* vFu = sFu;
-    volatile int* vFo = sFo;
-    volatile int* vFm0 = sFm0;
-    volatile int* vFm1 = sFm1;
-    volatile int* vMe = sMe;
-    volatile int* vMu = sMu;
-    volatile int* vMlo = sMlo;
-    volatile int* vMhi = sMhi;
+  // Per rank, in registers (rank r in lane r % 64, slot r / 64 of RPL
+  // slots; RPL = 1 up to 64 ranks): its load, its donor cursor (the first
+  // home expert it has not given away entirely) and the slots and moves
+  // already taken from that expert.  A donor gives its experts in
+  // ascending order, so every expert past the cursor is untouched and a
+  // fill reads nothing but T_e; sTaken and sMcnt are only written here.
+  auto fills = [&](auto rpl_tag) {
+    constexpr int RPL = decltype(rpl_tag)::value;
     const uint64_t lt = lanemask_lt();
+    int ld[RPL], cur[RPL], ctk[RPL], cmc[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int r = lane + kWave * i;
+      ld[i] = r < R ? sLoad0[r] : 0;
+      cur[i] = r * n;
+      ctk[i] = 0;
+      cmc[i] = 0;
+    }
     int nm = 0, nf = 0, err = 0;
     for (int iter = 0; iter < R; ++iter) {
       // receiver: lowest-id rank that is underloaded now
       int u = -1;
-      for (int r0 = 0; r0 < R; r0 += kWave) {
-        const int r = r0 + lane;
-        const uint64_t bal = __ballot(r < R && vLoad[r] < SK);
-        if (bal) { u = r0 + __ffsll((unsigned long long)bal) - 1; break; }
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        if (u < 0 && kWave * i < R) {
+          const uint64_t bal = __ballot(lane + kWave * i < R && ld[i] < SK);
+          if (bal) u = kWave * i + __ffsll((unsigned long long)bal) - 1;
+        }
       }
       if (u < 0) break;
       // donor: largest load, lowest id on ties
-      int best = -1, bestr = R;
-      for (int r = lane; r < R; r += kWave) {
-        const int l = vLoad[r];
-        if (l > best) { best = l; bestr = r; }
-      }
+      int lb = -1;
 #pragma unroll
-      for (int d = kWave / 2; d >= 1; d >>= 1) {
-        const int ob = __shfl_xor(best, d, kWave), orr = __shfl_xor(bestr, d, kWave);
-        if (ob > best || (ob == best && orr < bestr)) { best = ob; bestr = orr; }
+      for (int i = 0; i < RPL; ++i)
+        if (lane + kWave * i < R && ld[i] > lb) lb = ld[i];
+      const int mx = wave_max(lb);
+      if (mx <= SK) { err |= MOE_STATUS_INTERNAL; break; }
+      int o = -1;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        if (o < 0 && kWave * i < R) {
+          const uint64_t bal = __ballot(lane + kWave * i < R && ld[i] == mx);
+          if (bal) o = kWave * i + __ffsll((unsigned long long)bal) - 1;
+        }
       }
-      const int o = bestr;
-      if (best <= SK) { err |= MOE_STATUS_INTERNAL; break; }
-      const int need = SK - vLoad[u];
+      int lu = ld[0], co = cur[0], cot = ctk[0], com = cmc[0];
+#pragma unroll
+      for (int i = 1; i < RPL; ++i) {
+        if (i == u / kWave) lu = ld[i];
+        if (i == o / kWave) { co = cur[i]; cot = ctk[i]; com = cmc[i]; }
+      }
+      lu = wave_bcast(lu, u % kWave);
+      co = wave_bcast(co, o % kWave);
+      cot = wave_bcast(cot, o % kWave);
+      com = wave_bcast(com, o % kWave);
+      const int need = SK - lu;
       int d = need;
       const int m0 = nm;
-      int e0 = vCursor[o];
+      int e0 = co;
       const int eend = (o + 1) * n;
+      int ntk = 0, nmc = 0;                     // the new cursor's state
       // donor gives its home experts in ascending id, earliest slots first
       while (d > 0) {
         if (e0 >= eend) { err |= MOE_STATUS_INTERNAL; break; }
         const int e = e0 + lane;
         const bool in = e < eend;
-        const int rem = in ? vT[e] - vTaken[e] : 0;
+        const int tt = in ? sT[e] : 0;
+        const int tk = e == co ? cot : 0;
+        const int w = e == co ? com : 0;
+        const int rem = tt - tk;
         const int incl = wave_incl_scan(rem);
         const int take = in ? min(max(d - (incl - rem), 0), rem) : 0;
         const uint64_t mvb = __ballot(take > 0);
         if (take > 0) {
           const int idx = nm + (int)__popcll(mvb & lt);
-          const int lo = vTaken[e];
-          if (idx < M) { vMe[idx] = e; vMu[idx] = u; vMlo[idx] = lo; vMhi[idx] = lo + take; }
-          vTaken[e] = lo + take;
-          vMcnt[e] = vMcnt[e] + 1;
+          if (idx < M) { sMe[idx] = e; sMu[idx] = u; sMlo[idx] = tk; sMhi[idx] = tk + take; sMpos[idx] = w; }
+          sTaken[e] = tk + take;
+          sMcnt[e] = w + 1;
         }
         nm += (int)__popcll(mvb);
-        const int tot = __shfl(incl, kWave - 1, kWave);
+        const int tot = wave_bcast(incl, kWave - 1);
         d -= min(d, tot);
         if (d == 0) {
           const uint64_t left = __ballot(in && rem - take > 0);
-          e0 = left ? e0 + __ffsll((unsigned long long)left) - 1 : e0 + kWave;
+          if (left) {
+            const int L = __ffsll((unsigned long long)left) - 1;
+            e0 += L;
+            ntk = wave_bcast(tk + take, L);
+            nmc = wave_bcast(w + (take > 0 ? 1 : 0), L);
+          } else {
+            e0 += kWave;
+          }
         } else {
           e0 += kWave;
         }
       }
       if (err) break;
       if (nm > M) { err |= MOE_STATUS_INTERNAL; break; }
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        if (lane + kWave * i == o) { ld[i] -= need; cur[i] = e0; ctk[i] = ntk; cmc[i] = nmc; }
+        if (lane + kWave * i == u) ld[i] = SK;
+      }
       if (lane == 0) {
-        vCursor[o] = e0;
-        vLoad[o] = vLoad[o] - need;
-        vLoad[u] = SK;
-        vFu[nf] = u;
-        vFo[nf] = o;
-        vFm0[nf] = m0;
-        vFm1[nf] = nm;
-        vRecv[u] = nf;
+        sFo[nf] = o;
+        sFm0[nf] = m0;
+        sFm1[nf] = nm;
+        sRecv[u] = nf;
       }
       ++nf;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (lane == 0) {
       sNm = min(nm, M);
       sNf = nf;
       if (err) atomicOr(&sErr, err);
     }
+  };
+  if (wave == 0) {
+    if (R <= kWave) fills(IntTag<1>{});
+    else if (R <= 4 * kWave) fills(IntTag<4>{});
+    else fills(IntTag<MOE_MAX_R / kWave>{});
   }
   __syncthreads();
+  if (sErr & MOE_STATUS_INTERNAL) {
+    // Never expected (Theorem 1): a donor ran dry or the moves overflowed.
+    no_plan();
+    return;
+  }
   const int nm = sNm, nf = sNf;
 
-  // 4. CSR of moves per expert, ordered by receiver rank (ascending).
+  // 4. Moves per expert in fill order: CSR start of each expert.
   for (int e = tid; e < E; e += kPlanThreads) sMptr[e] = sMcnt[e];
   __syncthreads();
   block_excl_scan(sMptr, E, sScan);
-  if (wave == 0) {
-    volatile int* vRun = sRun;
-    for (int r = 0; r < R; ++r) {
-      const int f = sRecv[r];
-      if (f < 0) continue;
-      for (int m = sFm0[f] + lane; m < sFm1[f]; m += kWave) {
-        const int e = sMe[m];
-        const int k = vRun[e];
-        vRun[e] = k + 1;
-        sMpos[m] = sMptr[e] + k;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-  __syncthreads();
-  // experts that have consumers (ascending id), for reduce_grad
-  for (int e = tid; e < E; e += kPlanThreads) sRun[e] = sMcnt[e] > 0 ? 1 : 0;
-  __syncthreads();
-  const int ncons = block_excl_scan(sRun, E, sScan);
-  for (int e = tid; e < E; e += kPlanThreads)
-    if (sMcnt[e] > 0) a.cons[sRun[e]] = e;
-  if (tid == 0) a.misc[0] = ncons;
 
-  // 5. cu_seqlens of every rank; home and move route bases.
+  // 5. The last wave lists the experts that have moves (for reduce_grad).
+  // Then per rank: prefix of its home row lengths, of its prefetch rows and
+  // of its overflow rows (inference); cu_seqlens follows in closed form.
+  if (wave == kRouteWaves - 1) {
+    const uint64_t lt = lanemask_lt();
+    int k = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const bool has = e0 + lane < E && sMcnt[e0 + lane] > 0;
+      const uint64_t bal = __ballot(has);
+      if (has) a.cons[k + (int)__popcll(bal & lt)] = e0 + lane;
+      k += (int)__popcll(bal);
+    }
+    if (lane == 0) a.misc[0] = k;
+  }
   for (int r = wave; r < R; r += kRouteWaves) {
     const int f = sRecv[r];
     const int m0 = f >= 0 ? sFm0[f] : 0, m1 = f >= 0 ? sFm1[f] : 0;
     const int nred = m1 - m0;
-    const int o = f >= 0 ? sFo[f] : -1;
-    int32_t* cur = a.cu + int64_t(r) * (E + B + 1);
-    if (lane == 0) cur[0] = 0;
     int carry = 0;
-    for (int j0 = 0; j0 < E + B; j0 += kWave) {
-      const int j = j0 + lane;
-      int len = 0, mv = -1;
-      if (j < E) {
-        if (j / n == r) {
-          len = sT[j] - sTaken[j];
-        } else if (nred > B && j / n == o) {       // inference overflow row
-          for (int m = m0 + B; m < m1; ++m)
-            if (sMe[m] == j) { mv = m; break; }
-          if (mv >= 0) len = sMhi[mv] - sMlo[mv];
-        }
-      } else if (j < E + B) {
-        const int b = j - E;
-        if (b < nred) { mv = m0 + b; len = sMhi[mv] - sMlo[mv]; }
-      }
+    for (int t0 = 0; t0 < n; t0 += kWave) {
+      const int t = t0 + lane;
+      const int len = t < n ? sT[r * n + t] - sTaken[r * n + t] : 0;
       const int incl = wave_incl_scan(len);
-      const int start = carry + incl - len;
-      if (j < E + B) cur[j + 1] = carry + incl;
-      if (j < E && j / n == r) a.home_base[j] = r * SK + start - sTaken[j];
-      if (mv >= 0) a.cs_base[sMpos[mv]] = r * SK + start - sMlo[mv];
-      carry += __shfl(incl, kWave - 1, kWave);
+      if (t < n) sHpre[r * (n + 1) + t] = a.hpre[r * (n + 1) + t] = carry + incl - len;
+      carry += wave_bcast(incl, kWave - 1);
+    }
+    if (lane == 0) sHpre[r * (n + 1) + n] = a.hpre[r * (n + 1) + n] = carry;
+    carry = 0;
+    for (int b0 = 0; b0 < B; b0 += kWave) {
+      const int b = b0 + lane;
+      const int len = (b < B && b < nred) ? sMhi[m0 + b] - sMlo[m0 + b] : 0;
+      const int incl = wave_incl_scan(len);
+      if (b < B) sSpre[r * (B + 1) + b] = a.spre[r * (B + 1) + b] = carry + incl - len;
+      carry += wave_bcast(incl, kWave - 1);
+    }
+    if (lane == 0) sSpre[r * (B + 1) + B] = a.spre[r * (B + 1) + B] = carry;
+    carry = 0;
+    for (int m = m0 + B + lane; m - lane < m1; m += kWave) {     // overflow moves
+      const int len = m < m1 ? sMhi[m] - sMlo[m] : 0;
+      const int incl = wave_incl_scan(len);
+      if (m < m1) sOcum[m] = a.ocum[m] = carry + incl;
+      carry += wave_bcast(incl, kWave - 1);
     }
     if (lane == 0) {
-      if (carry != SK) atomicOr(&sErr, MOE_STATUS_INTERNAL);
-      if (a.mode == MOE_MODE_TRAIN && nred > B) atomicOr(&sErr, MOE_STATUS_CAPACITY);
+      sOt[r] = carry;
+      a.rinfo[3 * r + 0] = carry;                 // overflow rows
+      a.rinfo[3 * r + 1] = m0 + B;                // overflow moves [m0 + B, m1)
+      a.rinfo[3 * r + 2] = m1;
     }
   }
+  __syncthreads();
 
+  // overflow rows of rank r below weight row j: prefix over its overflow
+  // moves (ascending expert) with expert < j
+  auto over_below = [&](int r, int j) {
+    const int f = sRecv[r];
+    if (f < 0) return 0;
+    const int lo0 = sFm0[f] + B, hi0 = sFm1[f];
+    if (hi0 <= lo0) return 0;
+    int lo = lo0, hi = hi0;                                  // first move with e >= j
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sMe[mid] < j) lo = mid + 1; else hi = mid;
+    }
+    return lo > lo0 ? sOcum[lo - 1] : 0;
+  };
+  // rows of rank r before weight row j (j in [0, E+B])
+  const bool infer = a.mode == MOE_MODE_INFER;
+  auto cu_at = [&](int r, int j) {
+    if (j <= E) {
+      const int t = min(max(j - r * n, 0), n);
+      return sHpre[r * (n + 1) + t] + (infer ? over_below(r, j) : 0);
+    }
+    return sHpre[r * (n + 1) + n] + sOt[r] + sSpre[r * (B + 1) + (j - E)];
+  };
+  if (C == 0) {
+    // No slots: k_route does not run, so cu_seqlens is written here (with
+    // slots, k_route writes it from the exported per-rank prefixes).
+    const int W = E + B + 1;
+    for (int i = tid; i < R * W; i += kPlanThreads) a.cu[i] = cu_at(i / W, i % W);
+  }
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int h = e / n;
+    a.home_base[e] = h * SK + cu_at(h, e) - sTaken[e];
+  }
+  for (int m = tid; m < nm; m += kPlanThreads) {
+    const int u = sMu[m], f = sRecv[u], b = m - sFm0[f];
+    const int row_start = b < B ? cu_at(u, E + b) : cu_at(u, sMe[m]);
+    const int pos = sMptr[sMe[m]] + sMpos[m];
+    a.cs_base[pos] = u * SK + row_start - sMlo[m];
+    a.cs_lo[pos] = sMlo[m];
+    a.cs_hi[pos] = sMhi[m];
+    a.cs_dst[pos] = u;
+    a.cs_b[pos] = b;
+    a.moves[4 * m + 0] = sMe[m];
+    a.moves[4 * m + 1] = u;
+    a.moves[4 * m + 2] = sMlo[m];
+    a.moves[4 * m + 3] = sMhi[m];
+  }
+  for (int r = tid; r < R; r += kPlanThreads) {
+    const int f = sRecv[r];
+    const int nred = f >= 0 ? sFm1[f] - sFm0[f] : 0;
+    if (cu_at(r, E + B) != SK) atomicOr(&sErr, MOE_STATUS_INTERNAL);
+    if (a.mode == MOE_MODE_TRAIN && nred > B) atomicOr(&sErr, MOE_STATUS_CAPACITY);
+    a.n_red[r] = nred;
+    a.src_rank[r] = f >= 0 ? sFo[f] : -1;
+  }
   __syncthreads();
   if (sErr & MOE_STATUS_INTERNAL) {
     // Never expected (Theorem 1); keep every later step inside its buffers.
     for (int64_t i = tid; i < int64_t(R) * (E + B + 1); i += kPlanThreads) a.cu[i] = 0;
+    __syncthreads();
   }
 
-  // 6. Outputs and route tables.
+  // 6. Remaining outputs and route tables.
   for (int e = tid; e < E; e += kPlanThreads) {
     a.counts[e] = sT[e];
     a.taken[e] = sTaken[e];
     a.mptr[e] = sMptr[e];
     a.mcnt[e] = sMcnt[e];
-  }
-  for (int r = tid; r < R; r += kPlanThreads) {
-    const int f = sRecv[r];
-    a.load0[r] = sLoad0[r];
-    a.n_red[r] = f >= 0 ? sFm1[f] - sFm0[f] : 0;
-    a.src_rank[r] = f >= 0 ? sFo[f] : -1;
   }
   for (int64_t i = tid; i < int64_t(R) * B; i += kPlanThreads) {
     const int r = (int)(i / B), b = (int)(i % B);
@@ -408,17 +485,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     int e = -1;
     if (f >= 0 && b < sFm1[f] - sFm0[f]) e = sMe[sFm0[f] + b];
     a.slot_expert[i] = e;
-  }
-  for (int m = tid; m < nm; m += kPlanThreads) {
-    a.moves[4 * m + 0] = sMe[m];
-    a.moves[4 * m + 1] = sMu[m];
-    a.moves[4 * m + 2] = sMlo[m];
-    a.moves[4 * m + 3] = sMhi[m];
-    const int pos = sMpos[m];
-    a.cs_lo[pos] = sMlo[m];
-    a.cs_hi[pos] = sMhi[m];
-    a.cs_dst[pos] = sMu[m];
-    a.cs_b[pos] = m - sFm0[sRecv[sMu[m]]];
   }
   __syncthreads();
   if (tid == 0) {
@@ -434,99 +500,192 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 //   p >= taken[e]: home_base[e] + p          (stays on the home rank)
 //   otherwise:     cs_base[q] + p  for the move q of e with lo <= p < hi.
 // ---------------------------------------------------------------------------
+// With kCsrLds the move tables are staged in LDS as well (when they fit).
+// Every global read a workgroup needs before its first pass (its first 8
+// rounds of ids, the status, the per-expert tables and its chunk prefix) is
+// issued up front, so they share one memory round trip.
+template <bool kCsrLds>
 __global__ __launch_bounds__(kPlanThreads) void k_route(PlanArgs a) {
-  extern __shared__ int s_cnt[];  // [16][E]
-  const int E = a.E;
-  const int lane = lane_id(), w = threadIdx.x / kWave;
+  constexpr int kEPer = MOE_MAX_E / kPlanThreads;            // experts per thread
+  constexpr int kMPer = (MOE_MAX_E + MOE_MAX_R + kPlanThreads - 1) / kPlanThreads;
+  extern __shared__ int s_cnt[];  // [16][E], then the per-expert tables
+  const int E = a.E, M = a.M;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const uint64_t lt = lanemask_lt();
   const int64_t base = int64_t(blockIdx.x) * kRouteWaves * a.L + int64_t(w) * a.L;
   const int64_t lim = min<int64_t>(a.N, base + a.L);
-  const int st = a.status[2];
-  if (st & (MOE_STATUS_BAD_ID | MOE_STATUS_UNBALANCED | MOE_STATUS_INTERNAL)) {
-    for (int64_t i = base + lane; i < lim; i += kWave) a.route[i] = -1;
-    return;
-  }
   int* cnt = s_cnt + w * E;
   int* s_taken = s_cnt + kRouteWaves * E;     // [E] LDS copies of the
   int* s_home = s_taken + E;                  // [E] per-expert route tables
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    s_taken[e] = a.taken[e];
-    s_home[e] = a.home_base[e];
-  }
-  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // pass A: per-wave counts
-  for (int64_t b0 = base; b0 < lim; b0 += 8 * kWave) {
-    int ids8[8];
+  int* s_mptr = s_home + E;                   // [E]  (kCsrLds only)
+  int* s_mcnt = s_mptr + E;                   // [E]
+  int* s_lo = s_mcnt + E;                     // [M]
+  int* s_hi = s_lo + M;                       // [M]
+  int* s_base = s_hi + M;                     // [M]
+
+  auto load8 = [&](int64_t b0, int* ids8) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t i = b0 + u * kWave + lane;
       ids8[u] = i < lim ? a.ids[i] : E;
     }
+  };
+  int first[8];
+  load8(base, first);
+  const int st = a.status[2];
+  int t_taken[kEPer], t_home[kEPer], t_mptr[kEPer], t_mcnt[kEPer], t_cc[kEPer];
+  const int32_t* ccp = a.cc + int64_t(blockIdx.x) * E;
+#pragma unroll
+  for (int k = 0; k < kEPer; ++k) {
+    const int e = tid + k * kPlanThreads;
+    if (e < E) {
+      t_taken[k] = a.taken[e];
+      t_home[k] = a.home_base[e];
+      t_cc[k] = ccp[e];
+      if (kCsrLds) { t_mptr[k] = a.mptr[e]; t_mcnt[k] = a.mcnt[e]; }
+    }
+  }
+  int t_lo[kMPer], t_hi[kMPer], t_base[kMPer];
+  if (kCsrLds) {
+#pragma unroll
+    for (int k = 0; k < kMPer; ++k) {
+      const int q = tid + k * kPlanThreads;
+      if (q < M) { t_lo[k] = a.cs_lo[q]; t_hi[k] = a.cs_hi[q]; t_base[k] = a.cs_base[q]; }
+    }
+  }
+  // This workgroup's share of cu_seqlens (all zero when there is no plan):
+  // rows of rank r before weight row j, from the per-rank prefixes of home
+  // rows, prefetch rows and overflow rows (inference) that k_plan exported.
+  auto write_cu = [&](bool ok) {
+    const int n = a.n, B = a.B, W = E + B + 1, tot = a.R * W;
+    const int per = (tot + gridDim.x - 1) / gridDim.x;
+    const int i0 = blockIdx.x * per, i1 = min(tot, i0 + per);
+    const bool infer = a.mode == MOE_MODE_INFER;
+    for (int i = i0 + tid; i < i1; i += kPlanThreads) {
+      int v = 0;
+      if (ok) {
+        const int r = i / W, j = i % W;
+        const int32_t* hp = a.hpre + r * (n + 1);
+        if (j <= E) {
+          v = hp[min(max(j - r * n, 0), n)];
+          if (infer) {
+            // overflow moves of r ascend in expert id: count those below j
+            const int lo0 = a.rinfo[3 * r + 1];
+            int lo = lo0, hi = a.rinfo[3 * r + 2];
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (a.moves[4 * mid] < j) lo = mid + 1; else hi = mid;
+            }
+            if (lo > lo0) v += a.ocum[lo - 1];
+          }
+        } else {
+          v = hp[n] + a.rinfo[3 * r] + a.spre[r * (B + 1) + (j - E)];
+        }
+      }
+      a.cu[i] = v;
+    }
+  };
+  if (st & (MOE_STATUS_BAD_ID | MOE_STATUS_UNBALANCED | MOE_STATUS_INTERNAL)) {
+    for (int64_t i = base + lane; i < lim; i += kWave) a.route[i] = -1;
+    write_cu(false);
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kEPer; ++k) {
+    const int e = tid + k * kPlanThreads;
+    if (e < E) {
+      s_taken[e] = t_taken[k];
+      s_home[e] = t_home[k];
+      if (kCsrLds) { s_mptr[e] = t_mptr[k]; s_mcnt[e] = t_mcnt[k]; }
+    }
+  }
+  if (kCsrLds) {
+#pragma unroll
+    for (int k = 0; k < kMPer; ++k) {
+      const int q = tid + k * kPlanThreads;
+      if (q < M) { s_lo[q] = t_lo[k]; s_hi[q] = t_hi[k]; s_base[q] = t_base[k]; }
+    }
+  }
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // pass A: per-wave counts (LDS atomics; lanes sharing a key serialise)
+  auto count8 = [&](const int* ids8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if ((unsigned)ids8[u] < (unsigned)E) atomicAdd(&cnt[ids8[u]], 1);
+  };
+  count8(first);
+  for (int64_t b0 = base + 8 * kWave; b0 < lim; b0 += 8 * kWave) {
+    int ids8[8];
+    load8(b0, ids8);
+    count8(ids8);
+  }
+  write_cu(true);
+  __syncthreads();
+  // exclusive prefix over the 16 waves, on top of the chunk's prefix
+#pragma unroll
+  for (int k = 0; k < kEPer; ++k) {
+    const int e = tid + k * kPlanThreads;
+    if (e < E) {
+      int run = t_cc[k];
+      for (int ww = 0; ww < kRouteWaves; ++ww) {
+        const int v = s_cnt[ww * E + e];
+        s_cnt[ww * E + e] = run;
+        run += v;
+      }
+    }
+  }
+  __syncthreads();
+  // pass B: ranks and destinations
+  auto route8 = [&](int64_t b0, const int* ids8) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
+      const int64_t i = b0 + u * kWave + lane;
       const int key = ids8[u];
       const uint64_t act = __ballot(key < E);
+      if (act == 0) continue;
       const uint64_t m = match_any(key, a.nbits, act);
+      if (key < E) {
+        const int p = cnt[key] + (int)__popcll(m & lt);
+        int dest = -1;
+        if (p >= s_taken[key]) {
+          dest = s_home[key] + p;
+        } else if (kCsrLds) {
+          const int q0 = s_mptr[key], q1 = q0 + s_mcnt[key];
+          for (int q = q0; q < q1; ++q)
+            if (p >= s_lo[q] && p < s_hi[q]) { dest = s_base[q] + p; break; }
+        } else {
+          const int q0 = a.mptr[key], q1 = q0 + a.mcnt[key];
+          for (int q = q0; q < q1; ++q)
+            if (p >= a.cs_lo[q] && p < a.cs_hi[q]) { dest = a.cs_base[q] + p; break; }
+        }
+        a.route[i] = dest;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (key < E && (m & lt) == 0) cnt[key] += (int)__popcll(m);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-  }
-  __syncthreads();
-  // exclusive prefix over the 16 waves, on top of the chunk's prefix
-  const int32_t* ccp = a.cc + int64_t(blockIdx.x) * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = ccp[e];
-    for (int ww = 0; ww < kRouteWaves; ++ww) {
-      const int v = s_cnt[ww * E + e];
-      s_cnt[ww * E + e] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  // pass B: ranks and destinations
-  for (int64_t b0 = base; b0 < lim; b0 += 8 * kWave) {
-   int ids8[8];
-#pragma unroll
-   for (int u = 0; u < 8; ++u) {
-     const int64_t i = b0 + u * kWave + lane;
-     ids8[u] = i < lim ? a.ids[i] : E;
-   }
-#pragma unroll
-   for (int u = 0; u < 8; ++u) {
-    const int64_t i = b0 + u * kWave + lane;
-    const int key = ids8[u];
-    const uint64_t act = __ballot(key < E);
-    const uint64_t m = match_any(key, a.nbits, act);
-    if (key < E) {
-      const int p = cnt[key] + (int)__popcll(m & lt);
-      int dest = -1;
-      if (p >= s_taken[key]) {
-        dest = s_home[key] + p;
-      } else {
-        const int q0 = a.mptr[key], q1 = q0 + a.mcnt[key];
-        for (int q = q0; q < q1; ++q)
-          if (p >= a.cs_lo[q] && p < a.cs_hi[q]) { dest = a.cs_base[q] + p; break; }
-      }
-      a.route[i] = dest;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (key < E && (m & lt) == 0) cnt[key] += (int)__popcll(m);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-   }
+  };
+  route8(base, first);
+  for (int64_t b0 = base + 8 * kWave; b0 < lim; b0 += 8 * kWave) {
+    int ids8[8];
+    load8(b0, ids8);
+    route8(b0, ids8);
   }
 }
 
 static size_t plan_lds_bytes(const moe_cfg* c, const PlanLayout& L) {
-  return sizeof(int) * (size_t(5) * c->E + size_t(8) * c->R + size_t(5) * L.M + kPlanThreads + 32);
+  // the k_plan LDS layout: 4 arrays of E, 5 of R, 6 of M, R(n+1), R(B+1), scan scratch
+  const size_t E = c->E, R = c->R, n = E / R, B = c->B;
+  return sizeof(int) * (4 * E + 5 * R + 6 * size_t(L.M) + R * (n + 1) + R * (B + 1) +
+                        kPlanThreads + 32);
 }
 
 }  // namespace moonep
@@ -576,15 +735,34 @@ extern "C" int moe_plan_run(const moe_cfg* cfg, const int32_t* topk_ids, const m
   a.cs_hi = ws_i32(ws, L.off_cs_hi); a.cs_base = ws_i32(ws, L.off_cs_base);
   a.cs_dst = ws_i32(ws, L.off_cs_dst); a.cs_b = ws_i32(ws, L.off_cs_b);
   a.cons = ws_i32(ws, L.off_cons); a.misc = ws_i32(ws, L.off_misc);
+  a.hpre = ws_i32(ws, L.off_hpre); a.spre = ws_i32(ws, L.off_spre);
+  a.rinfo = ws_i32(ws, L.off_rinfo); a.ocum = ws_i32(ws, L.off_ocum);
 
   const size_t lds_count = sizeof(int) * cfg->E;
   const size_t lds_plan = plan_lds_bytes(cfg, L);
   const size_t lds_route = sizeof(int) * size_t(kRouteWaves + 2) * cfg->E;
+  const size_t lds_route_csr = lds_route + sizeof(int) * (size_t(2) * cfg->E + size_t(3) * L.M);
+  const bool csr_lds = lds_route_csr <= kMaxLds;
   if ((rc = allow_lds(k_plan, lds_plan)) != MOE_OK) return rc;
-  if ((rc = allow_lds(k_route, lds_route)) != MOE_OK) return rc;
-  if (L.C > 0) hipLaunchKernelGGL(k_count, dim3(L.C), dim3(kPlanThreads), lds_count, stream, a);
+  if (csr_lds) {
+    if ((rc = allow_lds(k_route<true>, lds_route_csr)) != MOE_OK) return rc;
+  } else {
+    if ((rc = allow_lds(k_route<false>, lds_route)) != MOE_OK) return rc;
+  }
+  if (L.C > 0) {
+    hipLaunchKernelGGL(k_count, dim3(L.C), dim3(kPlanThreads), lds_count, stream, a);
+    hipLaunchKernelGGL(k_colscan, dim3((cfg->E + kWave - 1) / kWave), dim3(kPlanThreads), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  }
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), lds_plan, stream, a);
-  if (L.C > 0) hipLaunchKernelGGL(k_route, dim3(L.C), dim3(kPlanThreads), lds_route, stream, a);
+  if (L.C > 0) {
+    if (csr_lds)
+      hipLaunchKernelGGL((k_route<true>), dim3(L.C), dim3(kPlanThreads), lds_route_csr, stream, a);
+    else
+      hipLaunchKernelGGL((k_route<false>), dim3(L.C), dim3(kPlanThreads), lds_route, stream, a);
+  }
   return hip_status();
 }
 
