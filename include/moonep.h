@@ -12,9 +12,16 @@
  *   moe_grouped_gemm_wgrad  fp32 weight gradients of the grouped GEMM
  *   moe_reduce_grad      fold prefetch-slot gradients into home rows
  *
+ * and its data backward:
+ *
+ *   moe_combine_backward    gradients of combine: permuted dy and gate grads
+ *   moe_grouped_gemm_dgrad  dxperm = dy @ W^T over the same rows
+ *   moe_dispatch_backward   sum each token's K permuted gradient rows
+ *
  * Sources: "Kimi K3 模型结构（8）：训练并行，MoonEP 与四类等待" (blog.javazero.top),
  * "Moonshot AI 开源 MoonEP" (feinterview), "MoonEP : l'équilibrage parfait"
- * (mkdocs.reaper.mx); each entry point cites the passage that defines it.
+ * (mkdocs.reaper.mx), "大规模 LLM 训练系统研究账本" (llm-atlas); each entry
+ * point cites the passage that defines it.
  *
  * Conventions for every entry point:
  *  - every pointer argument is a DEVICE pointer unless stated otherwise, and
@@ -65,7 +72,9 @@ enum {
   MOE_STATUS_INTERNAL = 8    /* a planner invariant failed                  */
 };
 
-/* Limits checked on the host (MOE_ELIMIT beyond them). */
+/* Limits checked on the host (MOE_ELIMIT beyond them).  Besides these:
+ * R*S*K < 2^31 slots, one weight matrix H*Hp*2 bytes < 4 GiB and one rank's
+ * permuted rows S*K*max(H, Hp)*2 bytes < 4 GiB. */
 #define MOE_MAX_E 2048
 #define MOE_MAX_R 1024
 #define MOE_MAX_K 64
@@ -151,8 +160,8 @@ int moe_dispatch(const moe_cfg *cfg, const moe_plan *plan, const moe_bf16 *x,
                  moe_bf16 *xperm, hipStream_t stream);
 
 /*
- * Host only.  Bytes of scratch that moe_grouped_gemm and
- * moe_grouped_gemm_wgrad need in their `workspace` argument.
+ * Host only.  Bytes of scratch that moe_grouped_gemm, moe_grouped_gemm_dgrad
+ * and moe_grouped_gemm_wgrad need in their `workspace` argument.
  */
 int moe_gemm_workspace_size(const moe_cfg *cfg, size_t *bytes_out);
 
@@ -213,6 +222,50 @@ int moe_grouped_gemm_wgrad(const moe_cfg *cfg, const moe_plan *plan,
  */
 int moe_reduce_grad(const moe_cfg *cfg, const moe_plan *plan, float *grad_home,
                     float *grad_pref, hipStream_t stream);
+
+/*
+ * Gradients of combine ("大规模 LLM 训练系统研究账本" §9.5: the MoE backward
+ * works on the permuted layout; the gradient of the gate-weighted sum in
+ * "Kimi K3 模型结构（8）", 在线规划、零拷贝、静态 shape).  For every token t
+ * and k with q = route[t*K + k] >= 0:
+ *   dy[q]          = bf16( gates[t][k] * dout[t] )   (exact product, rounded once)
+ *   dgates[t][k]   = sum_h dout[t][h] * y[q][h]      (fp32)
+ * dgates[t][k] = 0 for routes of -1.  dout [R*S][Hp] bf16, y [R][S*K][Hp]
+ * bf16 (the forward GEMM output), gates [R*S][K] fp32, dy [R][S*K][Hp] bf16,
+ * dgates [R*S][K] fp32.  Rows of dy no route names are not written.
+ */
+int moe_combine_backward(const moe_cfg *cfg, const moe_plan *plan,
+                         const moe_bf16 *dout, const moe_bf16 *y,
+                         const float *gates, moe_bf16 *dy, float *dgates,
+                         hipStream_t stream);
+
+/*
+ * Data gradient of the grouped GEMM ("大规模 LLM 训练系统研究账本" §9.5: the
+ * group GEMM backward runs over the rows that dispatch laid out).  For ranks
+ * r in [rank_begin, rank_end) and rows j with cu_seqlens[r][j] <
+ * cu_seqlens[r][j+1]:
+ *   dxperm[r][cu[j]:cu[j+1]] = bf16( dy[r][cu[j]:cu[j+1]] @ W(r, j)^T )
+ * with W(r, j) as for moe_grouped_gemm; fp32 accumulation, one rounding.
+ * dy [R][S*K][Hp], dxperm [R][S*K][H].  Rows outside the listed ranks are
+ * not written.  `workspace` as for moe_grouped_gemm.
+ */
+int moe_grouped_gemm_dgrad(const moe_cfg *cfg, const moe_bf16 *dy,
+                           const moe_bf16 *w_home, const moe_bf16 *w_pref,
+                           const int32_t *cu_seqlens, moe_bf16 *dxperm,
+                           int32_t rank_begin, int32_t rank_end,
+                           void *workspace, hipStream_t stream);
+
+/*
+ * Gradient of dispatch ("大规模 LLM 训练系统研究账本" §9.5, as for
+ * moe_combine_backward): every token's input gradient is the sum of the
+ * gradients of its K permuted copies,
+ *   dx[t] = bf16( sum_{k ascending} dxperm[route[t*K + k]] )
+ * accumulated in fp32.  dxperm [R][S*K][H] bf16, dx [R*S][H] bf16.  Routes
+ * of -1 contribute nothing.
+ */
+int moe_dispatch_backward(const moe_cfg *cfg, const moe_plan *plan,
+                          const moe_bf16 *dxperm, moe_bf16 *dx,
+                          hipStream_t stream);
 
 /* Host only.  Static text for a MOE_* return code. */
 const char *moe_strerror(int code);

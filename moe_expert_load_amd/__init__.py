@@ -21,7 +21,8 @@ PLAN_FIELDS = ("counts", "load0", "route", "cu_seqlens", "slot_expert",
 ENTRY_POINTS = ("moe_plan_sizes", "moe_plan_run", "moe_prefetch_weight",
                 "moe_dispatch", "moe_gemm_workspace_size", "moe_grouped_gemm",
                 "moe_combine", "moe_grouped_gemm_wgrad", "moe_reduce_grad",
-                "moe_strerror")
+                "moe_combine_backward", "moe_grouped_gemm_dgrad",
+                "moe_dispatch_backward", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -67,6 +68,9 @@ def load(path=None):
         "moe_combine": [C, PL, P, P, P, P],
         "moe_grouped_gemm_wgrad": [C, PL, P, P, P, P, P, P],
         "moe_reduce_grad": [C, PL, P, P, P],
+        "moe_combine_backward": [C, PL, P, P, P, P, P, P],
+        "moe_grouped_gemm_dgrad": [C, P, P, P, P, P, I32, I32, P, P],
+        "moe_dispatch_backward": [C, PL, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -223,6 +227,42 @@ def moe_grouped_gemm_wgrad(cfg, plan, xperm, dy, grad_home, grad_pref, workspace
             _ptr(workspace, torch.uint8, moe_gemm_workspace_size(cfg), "workspace"),
             _stream(stream))
     _check(load().moe_grouped_gemm_wgrad(*args), "moe_grouped_gemm_wgrad")
+
+
+def moe_combine_backward(cfg, plan, dout, y, gates, dy, dgates, stream=None):
+    ntok = cfg.R * cfg.S
+    args = (ctypes.byref(cfg), plan.c,
+            _ptr(dout, torch.bfloat16, ntok * cfg.Hp, "dout"),
+            _ptr(y, torch.bfloat16, ntok * cfg.K * cfg.Hp, "y"),
+            _ptr(gates, torch.float32, ntok * cfg.K, "gates"),
+            _ptr(dy, torch.bfloat16, ntok * cfg.K * cfg.Hp, "dy"),
+            _ptr(dgates, torch.float32, ntok * cfg.K, "dgates"),
+            _stream(stream))
+    _check(load().moe_combine_backward(*args), "moe_combine_backward")
+
+
+def moe_grouped_gemm_dgrad(cfg, dy, w_home, w_pref, cu_seqlens, dxperm, rank_begin, rank_end,
+                           workspace, stream=None):
+    SK = cfg.S * cfg.K
+    hh = cfg.H * cfg.Hp
+    args = (ctypes.byref(cfg),
+            _ptr(dy, torch.bfloat16, cfg.R * SK * cfg.Hp, "dy"),
+            _ptr(w_home, torch.bfloat16, cfg.E * hh, "w_home"),
+            _ptr(w_pref, torch.bfloat16, cfg.R * cfg.B * hh, "w_pref") if cfg.B else None,
+            _ptr(cu_seqlens, torch.int32, cfg.R * (cfg.E + cfg.B + 1), "cu_seqlens"),
+            _ptr(dxperm, torch.bfloat16, cfg.R * SK * cfg.H, "dxperm"),
+            int(rank_begin), int(rank_end),
+            _ptr(workspace, torch.uint8, moe_gemm_workspace_size(cfg), "workspace"),
+            _stream(stream))
+    _check(load().moe_grouped_gemm_dgrad(*args), "moe_grouped_gemm_dgrad")
+
+
+def moe_dispatch_backward(cfg, plan, dxperm, dx, stream=None):
+    ntok = cfg.R * cfg.S
+    a = _ptr(dxperm, torch.bfloat16, ntok * cfg.K * cfg.H, "dxperm")
+    o = _ptr(dx, torch.bfloat16, ntok * cfg.H, "dx")
+    _check(load().moe_dispatch_backward(ctypes.byref(cfg), plan.c, a, o, _stream(stream)),
+           "moe_dispatch_backward")
 
 
 def moe_reduce_grad(cfg, plan, grad_home, grad_pref, stream=None):

@@ -35,6 +35,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// bf16 bits of the exact product a*b, rounded once (nearest, ties to even).
+// The fp32 product p can only land on a bf16 rounding midpoint when the
+// exact product differs from it by the residual e = fma(a, b, -p); then e
+// decides the side.  Otherwise rounding p gives the same bf16 as rounding
+// the exact product.
+__device__ __forceinline__ uint32_t mul_to_bf16(float a, float b) {
+  const float p = a * b;
+  const uint32_t u = __float_as_uint(p);
+  if ((u & 0xffffu) == 0x8000u && (u & 0x7fffffffu) < 0x7f800000u) {
+    const float e = fmaf(a, b, -p);
+    if (e != 0.f) return ((e > 0.f) == (p > 0.f)) ? (u >> 16) + 1u : (u >> 16);
+  }
+  return f32_to_bf16(p);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
@@ -62,6 +77,19 @@ __device__ __forceinline__ int wave_bcast(int v, int src) {
 
 __device__ __forceinline__ int wave_sum(int v) {
   return wave_bcast(wave_incl_scan(v), kWave - 1);
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#define MOONEP_DPPF(x, ctrl, rows) \
+  __int_as_float(MOONEP_DPP(0, __float_as_int(x), (ctrl), (rows)))
+  v += MOONEP_DPPF(v, 0x111, 0xf);
+  v += MOONEP_DPPF(v, 0x112, 0xf);
+  v += MOONEP_DPPF(v, 0x114, 0xf);
+  v += MOONEP_DPPF(v, 0x118, 0xf);
+  v += MOONEP_DPPF(v, 0x142, 0xa);
+  v += MOONEP_DPPF(v, 0x143, 0xc);
+#undef MOONEP_DPPF
+  return __int_as_float(wave_bcast(__float_as_int(v), kWave - 1));
 }
 
 __device__ __forceinline__ int wave_max(int v) {

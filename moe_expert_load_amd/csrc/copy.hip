@@ -1,5 +1,5 @@
 // HBM-bound steps: prefetch_weight, fused permute (dispatch), gate-weighted
-// combine and reduce_grad.  Every row moves as 16-byte vectors; a wave owns a
+// combine and reduce_grad, and the backward of combine and of dispatch.  Every row moves as 16-byte vectors; a wave owns a
 // token (dispatch, combine) so its K routes are read once and broadcast with
 // lane shuffles.
 //
@@ -8,7 +8,9 @@
 // combine multiplies each expert output by its own fp32 router weight);
 // "Moonshot AI 开源 MoonEP", 核心思想 (prefetch_weight fills rows [E, E+B);
 // reduce_grad folds each rank's slots of an expert into its home gradient and
-// zeroes the consumed slots).
+// zeroes the consumed slots); "大规模 LLM 训练系统研究账本" §9.5 (the MoE
+// backward keeps the permuted layout: the gradients of combine and dispatch
+// are the transposed maps of the forward ones).
 #include "common.hpp"
 #include "host.hpp"
 
@@ -78,12 +80,13 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
 // combine: one wave per token; out = sum_k g_k * y[route_k] in fp32, k
 // ascending, rounded once to bf16.  The rows of KB routes are loaded before
 // any of them is accumulated, so KB * CU 16-byte loads per lane are in
-// flight.
+// flight.  With kUnit every gate is 1: the backward of dispatch,
+// dx[t] = sum_k dxperm[route_k].
 // ---------------------------------------------------------------------------
 #ifndef MOONEP_COMBINE_KB
 #define MOONEP_COMBINE_KB 8
 #endif
-template <int CU, int KB>
+template <int CU, int KB, bool kUnit>
 __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
                                                  const float* __restrict__ gates,
                                                  const int32_t* __restrict__ route,
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
   if (t >= ntok) return;
   const int lane = lane_id();
   const int myroute = lane < K ? route[int64_t(t) * K + lane] : -1;
-  const float mygate = lane < K ? gates[int64_t(t) * K + lane] : 0.f;
+  const float mygate = kUnit ? 1.f : lane < K ? gates[int64_t(t) * K + lane] : 0.f;
   for (int c0 = 0; c0 < hv; c0 += kWave * CU) {
     float acc[CU][8];
 #pragma unroll
@@ -139,6 +142,74 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// combine backward: one wave per token.  For each k,
+//   dy[route_k] = g_k * dout[t]               (bf16 of the exact product)
+//   dgates[t, k] = sum_h dout[t, h] * y[route_k, h]   (fp32, lanes then a
+//                                                     DPP tree)
+// dout is read once per token and each y row once; KB rows are in flight.
+// ---------------------------------------------------------------------------
+template <int CU, int KB>
+__global__ __launch_bounds__(256) void k_combine_bwd(const u32x4* __restrict__ dout,
+                                                     const u32x4* __restrict__ y,
+                                                     const float* __restrict__ gates,
+                                                     const int32_t* __restrict__ route,
+                                                     u32x4* __restrict__ dy,
+                                                     float* __restrict__ dgates, int ntok, int K,
+                                                     int hv) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;   // whole waves leave together
+  if (t >= ntok) return;
+  const int lane = lane_id();
+  const int myroute = lane < K ? route[int64_t(t) * K + lane] : -1;
+  const float mygate = lane < K ? gates[int64_t(t) * K + lane] : 0.f;
+  float mydot = 0.f;                                    // lane k: dgates[t, k]
+  for (int c0 = 0; c0 < hv; c0 += kWave * CU) {
+    u32x4 d[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      d[u] = c < hv ? __builtin_nontemporal_load(dout + int64_t(t) * hv + c) : u32x4{0, 0, 0, 0};
+    }
+    for (int k0 = 0; k0 < K; k0 += KB) {
+      u32x4 v[KB][CU];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int src = wave_bcast(myroute, min(k0 + kb, K - 1));
+        const bool ok = k0 + kb < K && src >= 0;
+        const u32x4* row = y + int64_t(ok ? src : 0) * hv;
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int c = c0 + u * kWave + lane;
+          v[kb][u] = (ok && c < hv) ? __builtin_nontemporal_load(row + c) : u32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (k0 + kb >= K) break;                        // uniform
+        const int dst = wave_bcast(myroute, k0 + kb);
+        const float g = __int_as_float(wave_bcast(__float_as_int(mygate), k0 + kb));
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int c = c0 + u * kWave + lane;
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float dl = bf16_lo(d[u][q]), dh = bf16_hi(d[u][q]);
+            part = fmaf(dl, bf16_lo(v[kb][u][q]), part);
+            part = fmaf(dh, bf16_hi(v[kb][u][q]), part);
+            o[q] = mul_to_bf16(g, dl) | (mul_to_bf16(g, dh) << 16);
+          }
+          if (dst >= 0 && c < hv) dy[int64_t(dst) * hv + c] = o;
+        }
+        const float s = wave_sum_f(part);
+        if (lane == k0 + kb) mydot += s;
+      }
+    }
+  }
+  if (lane < K) dgates[int64_t(t) * K + lane] = mydot;
 }
 
 // ---------------------------------------------------------------------------
@@ -260,13 +331,59 @@ extern "C" int moe_combine(const moe_cfg* cfg, const moe_plan* plan, const moe_b
   const dim3 grid((ntok + 3) / 4), block(256);
   const u32x4* ys = reinterpret_cast<const u32x4*>(y);
   u32x4* od = reinterpret_cast<u32x4*>(out);
-#define MOE_COMBINE(N)                                                                   \
-  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB>), grid, block, 0, stream, ys, gates, \
+#define MOE_COMBINE(N)                                                                          \
+  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB, false>), grid, block, 0, stream, ys, gates, \
                      plan->route, od, ntok, cfg->K, hv)
   if (cu <= 1) MOE_COMBINE(1);
   else if (cu <= 2) MOE_COMBINE(2);
   else MOE_COMBINE(4);
 #undef MOE_COMBINE
+  return hip_status();
+}
+
+extern "C" int moe_combine_backward(const moe_cfg* cfg, const moe_plan* plan, const moe_bf16* dout,
+                                    const moe_bf16* y, const float* gates, moe_bf16* dy,
+                                    float* dgates, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  const int ntok = cfg->R * cfg->S;
+  if (ntok == 0) return MOE_OK;
+  if (!plan || !plan->route || !dout || !y || !gates || !dy || !dgates) return MOE_EINVAL;
+  const int hv = cfg->Hp / 8;
+  const int cu = (hv + kWave - 1) / kWave;
+  const dim3 grid((ntok + 3) / 4), block(256);
+  const u32x4* ds = reinterpret_cast<const u32x4*>(dout);
+  const u32x4* ys = reinterpret_cast<const u32x4*>(y);
+  u32x4* dd = reinterpret_cast<u32x4*>(dy);
+#define MOE_COMBINE_BWD(N)                                                                \
+  hipLaunchKernelGGL((k_combine_bwd<N, 4>), grid, block, 0, stream, ds, ys, gates, plan->route, \
+                     dd, dgates, ntok, cfg->K, hv)
+  if (cu <= 1) MOE_COMBINE_BWD(1);
+  else if (cu <= 2) MOE_COMBINE_BWD(2);
+  else MOE_COMBINE_BWD(4);
+#undef MOE_COMBINE_BWD
+  return hip_status();
+}
+
+extern "C" int moe_dispatch_backward(const moe_cfg* cfg, const moe_plan* plan,
+                                     const moe_bf16* dxperm, moe_bf16* dx, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  const int ntok = cfg->R * cfg->S;
+  if (ntok == 0) return MOE_OK;
+  if (!plan || !plan->route || !dxperm || !dx) return MOE_EINVAL;
+  const int hv = cfg->H / 8;
+  const int cu = (hv + kWave - 1) / kWave;
+  const dim3 grid((ntok + 3) / 4), block(256);
+  const u32x4* xs = reinterpret_cast<const u32x4*>(dxperm);
+  u32x4* od = reinterpret_cast<u32x4*>(dx);
+#define MOE_UNDISPATCH(N)                                                                   \
+  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB, true>), grid, block, 0, stream, xs,    \
+                     (const float*)nullptr, plan->route, od, ntok, cfg->K, hv)
+  if (cu <= 1) MOE_UNDISPATCH(1);
+  else if (cu <= 2) MOE_UNDISPATCH(2);
+  else MOE_UNDISPATCH(4);
+#undef MOE_UNDISPATCH
   return hip_status();
 }
 

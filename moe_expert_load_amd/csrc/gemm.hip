@@ -46,7 +46,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int BM = 256, BN = 256;
 constexpr int kGemmThreads = 256;
 
-enum { MODE_FWD = 0, MODE_WGRAD = 1 };
+enum { MODE_FWD = 0, MODE_WGRAD = 1, MODE_DGRAD = 2 };
 
 struct WorkItem {
   int32_t r, j, row0, rows;  // rank, weight row, first xperm row (absolute), row count
@@ -57,7 +57,7 @@ struct GemmArgs {
   const uint16_t* w_home;
   const uint16_t* w_pref;
   const uint16_t* dy;
-  uint16_t* y;
+  uint16_t* y;                // forward output; the data gradient's output (dxperm)
   float* grad_home;
   float* grad_pref;
   const WorkItem* items;
@@ -209,9 +209,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wv >> 1, wn = wv & 1;
+  // Operand tiles: a "row tile" holds k-contiguous rows (forward A, and
+  // both operands of the data gradient), a "col tile" k-strided rows.
+  constexpr bool kRowA = MODE != MODE_WGRAD, kRowB = MODE == MODE_DGRAD;
   const int H = g.H, Hp = g.Hp;
-  const int ntm = MODE == MODE_FWD ? 1 : (H + BM - 1) / BM;
-  const int ntn = (Hp + BN - 1) / BN;
+  const int ntm = MODE == MODE_WGRAD ? (H + BM - 1) / BM : 1;
+  const int NOUT = MODE == MODE_DGRAD ? H : Hp;          // output columns
+  const int ntn = (NOUT + BN - 1) / BN;
   const int64_t total = int64_t(*g.nitems) * ntm * ntn;
   const int G = gridDim.x, per = G / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
@@ -226,13 +230,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     const int c = (4 * j + 2 * (G4 & 1) + ((li & 3) >> 1)) ^ (4 * (li >> 2));
     tr_off[j] = tr_k * 512 + c * 16 + 8 * (li & 1);
   }
-  // Row-tile MFMA reads (forward A): row = wm*128 + 32 i + lane%32,
+  // Row-tile MFMA reads: row = wm*128 (A) or wn*128 (B) + 32 i + lane%32,
   // chunk 2 s + lane/32.
-  int ra_off[BK / 16];
+  int ra_off[BK / 16], rb_off[BK / 16];
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) {
     const int row = lane & 31, kc = 2 * s + (lane >> 5);
-    ra_off[s] = (wm * 128 + row) * ROWB + ((kc ^ ((row >> RSH) & (CPR - 1))) << 4);
+    const int sw = (kc ^ ((row >> RSH) & (CPR - 1))) << 4;
+    ra_off[s] = (wm * 128 + row) * ROWB + sw;
+    rb_off[s] = (wn * 128 + row) * ROWB + sw;
   }
 
   for (int64_t q = 0;; ++q) {
@@ -243,18 +249,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     const int tm = rest / ntn, tn = rest % ntn;
     const WorkItem it = g.items[item];
     const int n0 = tn * BN, m0 = tm * BM;
-    const int KD = MODE == MODE_FWD ? H : it.rows;
+    const int KD = MODE == MODE_FWD ? H : MODE == MODE_DGRAD ? Hp : it.rows;
     // k-tiles, rounded up to whole passes over the stages: tiles past the
     // end load zeros (range-checked loads; ragged forward K is zeroed below)
     const int nk = ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
 
     // Operand A: forward = xperm rows of the segment (row tile); weight
-    // gradient = the same rows read as x^T (col tile over h).
-    // Operand B: forward = weight W(r, j) [H][Hp]; weight gradient = dy rows.
-    const uint16_t* Abase = g.xperm + int64_t(it.row0) * H;
+    // gradient = the same rows read as x^T (col tile over h); data gradient
+    // = dy rows (row tile over h').
+    // Operand B: forward = weight W(r, j) [H][Hp] (col tile); weight
+    // gradient = dy rows (col tile); data gradient = W(r, j) read as W^T,
+    // i.e. rows h of W with k = h' contiguous (row tile).
+    const int arow = MODE == MODE_DGRAD ? Hp : H;        // A row length
+    const uint16_t* Abase = (MODE == MODE_DGRAD ? g.dy : g.xperm) + int64_t(it.row0) * arow;
     const uint16_t* Bbase;
     uint32_t bbytes;
-    if (MODE == MODE_FWD) {
+    if (MODE != MODE_WGRAD) {
       Bbase = it.j < g.E ? g.w_home + int64_t(it.j) * H * Hp
                          : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
       bbytes = uint32_t(H) * Hp * 2;
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       Bbase = g.dy + int64_t(it.row0) * Hp;
       bbytes = uint32_t(it.rows) * Hp * 2;
     }
-    const u32x4 ra = make_rsrc(Abase, uint32_t(it.rows) * H * 2);
+    const u32x4 ra = make_rsrc(Abase, uint32_t(it.rows) * arow * 2);
     const u32x4 rb = make_rsrc(Bbase, bbytes);
 
     // Per-lane global byte offsets of this wave's load instructions.
@@ -270,18 +280,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
       const int t = wv * NI + u;
-      if (MODE == MODE_FWD) {
-        const int row = t * T::RPI + lane / CPR;
-        const int kc = (lane % CPR) ^ ((row >> RSH) & (CPR - 1));
-        goa[u] = uint32_t(row) * H * 2 + kc * 16;
-      } else {
-        const int row = t * 2 + (lane >> 5);
-        const int c = (lane & 31) ^ (4 * (row & 3));
-        goa[u] = uint32_t(row) * H * 2 + uint32_t(m0 + 8 * c) * 2;
-      }
-      const int row = t * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (row & 3));
-      gob[u] = uint32_t(row) * Hp * 2 + uint32_t(n0 + 8 * c) * 2;
+      // row tile: load t covers rows t*RPI .. +RPI, 16-byte chunks swizzled
+      const int rrow = t * T::RPI + lane / CPR;
+      const int rkc = (lane % CPR) ^ ((rrow >> RSH) & (CPR - 1));
+      // col tile: load t covers k rows 2t, 2t+1 of 256 columns
+      const int crow = t * 2 + (lane >> 5);
+      const int cc = (lane & 31) ^ (4 * (crow & 3));
+      if (kRowA) goa[u] = uint32_t(rrow) * arow * 2 + rkc * 16;
+      else goa[u] = uint32_t(crow) * H * 2 + uint32_t(m0 + 8 * cc) * 2;
+      if (kRowB) gob[u] = uint32_t(n0 + rrow) * Hp * 2 + rkc * 16;
+      else gob[u] = uint32_t(crow) * Hp * 2 + uint32_t(n0 + 8 * cc) * 2;
     }
 
     f32x16 acc[4][4];
@@ -297,10 +305,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       constexpr int S = decltype(S_)::value;
       unsigned char* As = stage_a<S>();
       unsigned char* Bs = stage_b<S>();
-      const uint32_t ka = MODE == MODE_FWD ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
-      const uint32_t kb = uint32_t(kt) * BK * Hp * 2;
+      const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * Hp * 2;
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
+        load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
+        load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
+      }
+    };
+    // Half h of those loads (A and B pieces u in [h*NI/2, (h+1)*NI/2)).
+    auto issue_part = [&](auto S_, int kt, int h) {
+      constexpr int S = decltype(S_)::value;
+      unsigned char* As = stage_a<S>();
+      unsigned char* Bs = stage_b<S>();
+      const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * Hp * 2;
+#pragma unroll
+      for (int u2 = 0; u2 < NI / 2; ++u2) {
+        const int u = h * (NI / 2) + u2;
         load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
         load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
       }
@@ -312,7 +334,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       const unsigned char* Bs = stage_b<S>();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (MODE == MODE_FWD) {
+        if (kRowA) {
           af[i] = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * 32 * ROWB));
         } else {
@@ -322,9 +344,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
-        bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
+        if (kRowB) {
+          bfr[j] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(Bs + rb_off[s] + j * 32 * ROWB));
+        } else {
+          const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
+          bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
+        }
       }
+    };
+    // One row of MFMA blocks (A fragment i against the 4 B fragments).
+    auto mfma_row = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
     auto mfma16 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
 #pragma unroll
@@ -337,7 +370,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     // fragments: one read between consecutive MFMAs keeps the matrix pipe fed
     // while the reads are in flight.
     auto interleave = [&]() {
-      constexpr int NR = MODE == MODE_FWD ? 12 : 16;
+      constexpr int NR = (kRowA ? 4 : 8) + (kRowB ? 4 : 8);   // LDS reads per substep
 #pragma unroll
       for (int x = 0; x < NR; ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -362,15 +395,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       constexpr int S = decltype(S_)::value;
       constexpr int SN = (S + 1) % kNST;
       unsigned char* As = stage_a<S>();
-      if (MODE == MODE_FWD && (kt + 1) * BK > H) {
-        // ragged K: the A chunks past H hold the next row's data -- zero
-        // them and re-read this substep's fragments
+      if (kRowA && (kt + 1) * BK > KD) {
+        // ragged K: row-tile chunks past the row length hold the next row's
+        // data -- zero them and re-read this substep's fragments
+        unsigned char* Bs = stage_b<S>();
         wait_vm<0>();
         barrier_lds();
         for (int x = tid; x < kTile / 16; x += kGemmThreads) {
           const int row = x / CPR, phys = x % CPR;
           const int kc = phys ^ ((row >> RSH) & (CPR - 1));
-          if (kt * BK + kc * 8 >= H) *reinterpret_cast<u32x4*>(As + x * 16) = u32x4{0, 0, 0, 0};
+          if (kt * BK + kc * 8 >= KD) {
+            *reinterpret_cast<u32x4*>(As + x * 16) = u32x4{0, 0, 0, 0};
+            if (kRowB) *reinterpret_cast<u32x4*>(Bs + x * 16) = u32x4{0, 0, 0, 0};
+          }
         }
         __syncthreads();
         read_frags(S_, 0, fa0, fb0);
@@ -389,17 +426,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         interleave();
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
-      if (kt + 1 < nk) {
-        // all waves are done with stage S once past this barrier: refill it
-        // with k-tile kt + kNST
-        publish(kt + 1);
-        if (kt + kNST < nk) issue(std::integral_constant<int, S>(), kt + kNST);
-      }
-      // last substep's MFMAs, substep 0 reads of the next stage (stale and
-      // unused after the last k-tile)
-      mfma16(fa1, fb1);
+      // Last substep: its fragments are in registers, so its 16 MFMAs cover
+      // the hand-over -- publish k-tile kt+1 (all waves are done with stage
+      // S past that barrier), read substep 0 of the next stage (stale and
+      // unused after the last k-tile) and refill stage S with k-tile
+      // kt + kNST -- instead of the matrix pipe idling through it.
+      mfma_row(fa1, fb1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) publish(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
       read_frags(std::integral_constant<int, SN>(), 0, fa0, fb0);
-      interleave();
+      mfma_row(fa1, fb1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + kNST < nk) issue_part(std::integral_constant<int, S>(), kt + kNST, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_row(fa1, fb1, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + kNST < nk) issue_part(std::integral_constant<int, S>(), kt + kNST, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_row(fa1, fb1, 3);
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     if (nk > 0) {                                               // then nk >= kNST
@@ -430,12 +476,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 
     // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
     // rows 8*(v/4) + 4*(l/32) + v%4 of its block for v = 0..15.
-    if (MODE == MODE_FWD) {
+    if (MODE != MODE_WGRAD) {
       // Per wave, two passes of 64 rows x 128 columns staged as bf16 in the
       // wave's own 16 KB stage array (256-byte rows), then whole 16-byte row
-      // chunks to global memory.
+      // chunks to global memory (rows of NOUT columns).
       unsigned char* Cs = epilogue_area(wv);
-      uint16_t* yb = g.y + int64_t(it.row0) * Hp;
+      uint16_t* yb = g.y + int64_t(it.row0) * NOUT;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         unsigned char* cbase = Cs + 4 * (lane >> 5) * 256 + (lane & 31) * 2;
@@ -460,8 +506,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
           const int rr = c >> 4, cc = c & 15;
           const int m = wm * 128 + half * 64 + rr;
           const int n = n0 + wn * 128 + cc * 8;
-          if (m < it.rows && n < Hp)
-            *reinterpret_cast<u32x4*>(yb + uint32_t(m) * Hp + n) =
+          if (m < it.rows && n < NOUT)
+            *reinterpret_cast<u32x4*>(yb + uint32_t(m) * NOUT + n) =
                 *reinterpret_cast<const u32x4*>(Cs + rr * 256 + cc * 16);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -470,21 +516,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       }
       __syncthreads();
     } else {
+      // fp32 gradient rows: per wave, four passes of 32 rows x 128 columns
+      // staged in the wave's own 16 KB stage array (512-byte rows), then
+      // whole 16-byte pieces (a wave writes two 512-byte row pieces per
+      // store) to global memory.
       float* out = it.j < g.E ? g.grad_home + int64_t(it.j) * H * Hp
                               : g.grad_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
+      unsigned char* Cs = epilogue_area(wv);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + 32 * j + (lane & 31);
-          if (n >= Hp) continue;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int h = m0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (h < H) out[uint32_t(h) * Hp + n] = acc[i][j][v];
+            const int rr = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            *reinterpret_cast<float*>(Cs + rr * 512 + (32 * j + (lane & 31)) * 4) = acc[i][j][v];
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 4
+        for (int c = lane; c < 32 * 32; c += kWave) {
+          const int rr = c >> 5, cc = c & 31;
+          const int h = m0 + wm * 128 + 32 * i + rr;
+          const int n = n0 + wn * 128 + cc * 4;
+          if (h < H && n < Hp)                     // written once: streaming store
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(Cs + rr * 512 + cc * 16),
+                                        reinterpret_cast<f32x4*>(out + uint32_t(h) * Hp + n));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
+      __syncthreads();
     }
   }
 }
@@ -584,17 +650,19 @@ static size_t gemm_ws_bytes(const moe_cfg* c) {
   return 256 + size_t(cap) * sizeof(WorkItem);
 }
 
+// The data gradient runs over the forward's work list (the same row tiles).
 static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hipStream_t stream) {
-  int rc;
-  if (mode == MODE_FWD) {
-    hipLaunchKernelGGL(k_sched<MODE_FWD>, dim3(1), dim3(1024), 0, stream, s);
-  } else {
+  if (mode == MODE_WGRAD) {
     hipLaunchKernelGGL(k_sched<MODE_WGRAD>, dim3(1), dim3(1024), 0, stream, s);
+  } else {
+    hipLaunchKernelGGL(k_sched<MODE_FWD>, dim3(1), dim3(1024), 0, stream, s);
   }
   int G = num_cus();
   G = std::max(8, G - G % 8);
   if (mode == MODE_FWD)
     hipLaunchKernelGGL((k_gemm<MODE_FWD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+  else if (mode == MODE_DGRAD)
+    hipLaunchKernelGGL((k_gemm<MODE_DGRAD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
   else
     hipLaunchKernelGGL((k_gemm<MODE_WGRAD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
   return hip_status();
@@ -635,6 +703,31 @@ extern "C" int moe_grouped_gemm(const moe_cfg* cfg, const moe_bf16* xperm, const
   g.items = s.items;
   g.nitems = s.nitems;
   return launch_gemm(MODE_FWD, cfg, g, s, stream);
+}
+
+extern "C" int moe_grouped_gemm_dgrad(const moe_cfg* cfg, const moe_bf16* dy, const moe_bf16* w_home,
+                                      const moe_bf16* w_pref, const int32_t* cu_seqlens,
+                                      moe_bf16* dxperm, int32_t rank_begin, int32_t rank_end,
+                                      void* workspace, hipStream_t stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (rank_begin < 0 || rank_end > cfg->R || rank_begin > rank_end) return MOE_EINVAL;
+  if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
+  if (!dy || !w_home || !cu_seqlens || !dxperm || !workspace) return MOE_EINVAL;
+  if (cfg->B > 0 && !w_pref) return MOE_EINVAL;
+  GemmArgs g{};
+  g.dy = dy; g.w_home = w_home; g.w_pref = w_pref; g.y = dxperm;
+  g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
+  SchedArgs s{};
+  s.cu = cu_seqlens;
+  s.nitems = reinterpret_cast<int32_t*>(workspace);
+  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
+  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
+  s.SK = cfg->S * cfg->K;
+  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
+  g.items = s.items;
+  g.nitems = s.nitems;
+  return launch_gemm(MODE_DGRAD, cfg, g, s, stream);
 }
 
 extern "C" int moe_grouped_gemm_wgrad(const moe_cfg* cfg, const moe_plan* plan,

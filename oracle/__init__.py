@@ -18,8 +18,11 @@ Sources (the pages this oracle is written from):
 * [MoonEP-fr] "MoonEP : l'équilibrage parfait" (mkdocs.reaper.mx) -- "Le
   théorème" (Théorème 1 and its lemma, Théorème 2), "La planification en
   ligne" (offline ILP as the yardstick).
-* [TSR] "TRAINING_SYSTEMS_RESEARCH" (llm-atlas) -- §6.1 (router -> dispatch ->
-  expert GEMM -> combine -> weighted sum) and §6.4 (proof structure).
+* [TSR] "TRAINING_SYSTEMS_RESEARCH" (llm-atlas), the page titled
+  "大规模 LLM 训练系统研究账本" -- §6.1 (router -> dispatch -> expert GEMM ->
+  combine -> weighted sum), §6.4 (proof structure) and §9.5 (the MoE
+  backward stays on the permuted layout; dispatch is redone to restore the
+  GEMM input).
 
 Modules:
 
@@ -27,7 +30,8 @@ Modules:
 * :mod:`oracle.plan`     -- histogram, stable slot ranks, the deterministic
   Theorem-1 construction, cu_seqlens and the route map.
 * :mod:`oracle.dataflow` -- dispatch, prefetch, grouped GEMM, combine,
-  weight-grad GEMM and reduce_grad, in float64.
+  weight-grad GEMM and reduce_grad, and the data backward (combine_backward,
+  dgrad, dispatch_backward), in float64.
 * :mod:`oracle.optimum`  -- minimum achievable max-redundancy on tiny inputs
   (brute force with a Hall-condition feasibility test, and a SciPy MILP), the
   per-rank lower bound and the Theorem-2 bound.

@@ -9,7 +9,9 @@ tolerances in the parity tests cover.
 
 Pinned by tests/test_oracle_dataflow.py: bit-copy invariants of permute and
 prefetch, closed forms with W[e] = c_e * I and constant gates, brute-force
-triple loops on tiny shapes, and known constants for reduce_grad.
+triple loops on tiny shapes, known constants for reduce_grad, and for the
+backward maps the adjoint identities <dout, F(x)> = <F^T(dout), x> with
+small-integer data (exact in bf16 and float64).
 """
 import numpy as np
 
@@ -191,3 +193,90 @@ def reduce_terms_abs(grad_home, grad_pref, plan, cfg):
 __all__ = ["dispatch", "prefetch", "weight_row", "grouped_gemm", "gemm_rows",
            "combine", "wgrad", "reduce_grad", "reduce_terms_abs",
            "segment_of_rows"]
+
+
+def combine_backward(dout_bits, y_bits, gates, plan, cfg):
+    """Gradients of combine with respect to y and to the gates.
+
+    combine is out[t] = sum_k g[t, k] * y[route[t*K + k]] ([K3-blog]
+    "在线规划、零拷贝、静态 shape"; [TSR] §6.1), so by the chain rule
+      dy[route[t*K + k]] = g[t, k] * dout[t]        (bf16, rounded once)
+      dgates[t, k]       = sum_h dout[t, h] * y[route[t*K + k], h]
+    [TSR] §9.5: the backward of the MoE layer works on the permuted layout.
+    The product g * dout of an fp32 and a bf16 value is exact in float64.
+    Returns (dy bits [R*S*K, H'], dgates float64 [R*S, K]); rows of dy that
+    no route names stay zero, and routes of -1 give dgates 0.
+    """
+    K = cfg.K
+    g = np.asarray(gates, np.float64).reshape(-1, K)
+    nt = g.shape[0]
+    route = plan.route.reshape(nt, K)
+    d = bf16.bits_to_f64(np.asarray(dout_bits, np.uint16))
+    y = np.asarray(y_bits, np.uint16)
+    dy = np.zeros((cfg.R * cfg.SK, cfg.Hp), np.uint16)
+    dg = np.zeros((nt, K), np.float64)
+    for k in range(K):
+        ok = route[:, k] >= 0
+        q = route[ok, k]
+        dy[q] = bf16.f64_to_bits(g[ok, k:k + 1] * d[ok])
+        dg[ok, k] = np.sum(d[ok] * bf16.bits_to_f64(y[q]), axis=1)
+    return dy, dg
+
+
+def dgrad(dy_bits, w_home_bits, w_pref_bits, plan, cfg, ranks=None):
+    """Data gradient of the grouped GEMM: dxperm[rows] = dy[rows] @ W(r, j)^T.
+
+    The grouped GEMM is y[rows of j] = xperm[rows] @ W(r, j) ([MoonEP-news]
+    "核心思想"), so its input gradient over the same rows is dy @ W^T;
+    [TSR] §9.5 keeps the backward on the rows dispatch laid out.  float64 on
+    exact bf16 values, rounded once.  Rows of ranks not in ``ranks`` stay 0.
+    """
+    R, SK, E, B = cfg.R, cfg.SK, cfg.E, cfg.B
+    dx = np.zeros((R * SK, cfg.H), np.uint16)
+    for r in (range(R) if ranks is None else ranks):
+        for j in range(E + B):
+            lo, hi = plan.cu_seqlens[r, j], plan.cu_seqlens[r, j + 1]
+            if hi == lo:
+                continue
+            d = bf16.bits_to_f64(dy_bits[r * SK + lo:r * SK + hi])
+            w = bf16.bits_to_f64(weight_row(w_home_bits, w_pref_bits, r, j, cfg))
+            dx[r * SK + lo:r * SK + hi] = bf16.f64_to_bits(d @ w.T)
+    return dx
+
+
+def dgrad_rows(rows, dy_bits, w_home_bits, w_pref_bits, plan, cfg):
+    """``dgrad`` for selected destination rows only (large shapes)."""
+    SK = cfg.SK
+    rows = np.asarray(rows, np.int64)
+    seg = np.empty(rows.size, np.int64)
+    for idx, q in enumerate(rows):
+        r, off = divmod(int(q), SK)
+        seg[idx] = np.searchsorted(plan.cu_seqlens[r], off, side="right") - 1
+    out = np.zeros((rows.size, cfg.H), np.uint16)
+    keys = (rows // SK) * (cfg.E + cfg.B) + seg
+    for key in np.unique(keys):
+        sel = np.nonzero(keys == key)[0]
+        r, j = divmod(int(key), cfg.E + cfg.B)
+        d = bf16.bits_to_f64(np.asarray(dy_bits[rows[sel]]))
+        w = bf16.bits_to_f64(weight_row(w_home_bits, w_pref_bits, r, j, cfg))
+        out[sel] = bf16.f64_to_bits(d @ w.T)
+    return out
+
+
+def dispatch_backward(dxperm_bits, plan, cfg):
+    """Gradient of dispatch: dx[t] = sum over k (ascending) of dxperm[route].
+
+    dispatch copies token t to its K destination rows ([K3-blog] "在线规划、
+    零拷贝、静态 shape"), so the gradient of token t is the sum of the
+    gradients of its copies ([TSR] §9.5).  float64, rounded once; routes of
+    -1 contribute nothing.
+    """
+    K = cfg.K
+    route = plan.route.reshape(-1, K)
+    nt = route.shape[0]
+    x = np.asarray(dxperm_bits, np.uint16)
+    acc = np.zeros((nt, cfg.H), np.float64)
+    for k in range(K):
+        ok = route[:, k] >= 0
+        acc[ok] += bf16.bits_to_f64(x[route[ok, k]])
+    return bf16.f64_to_bits(acc)

@@ -162,3 +162,134 @@ def test_reduce_grad_known_constants():
             else:
                 assert np.all(gp2[r, b] == (r + 1) * 1000 + b)   # untouched
     assert (plan.slot_expert >= 0).sum() == plan.n_redundant.sum()
+
+
+# ---------------------------------------------------------------------------
+# Backward of the data path.  Each backward map F^T is pinned to its forward
+# map F (pinned above) by the adjoint identity <dout, F(x)> = <F^T(dout), x>,
+# evaluated exactly: small-integer data and power-of-two gates keep every
+# product and sum exact in bf16 and float64.
+# ---------------------------------------------------------------------------
+def int_bits(g, shape, lo=-2, hi=2):
+    return bf16.f64_to_bits(g.integers(lo, hi + 1, size=shape).astype(np.float64))
+
+
+def f64(bits):
+    return bf16.bits_to_f64(bits)
+
+
+@pytest.mark.parametrize("shape", [W.TINY, W.TINY.with_(B=1, mode=1),
+                                   W.TINY.with_(R=2, E=8, K=3, S=10, B=4)])
+def test_combine_backward_adjoint_and_gate_gradient(shape):
+    g = np.random.default_rng(21)
+    cfg, ids, _, plan = tiny_setup(shape, seed=5)
+    nt, K = shape.tokens, shape.K
+    gates = (2.0 ** g.integers(-2, 2, size=(nt, K))).astype(np.float32)
+    y = int_bits(g, (shape.R * shape.SK, shape.Hp))
+    dout = int_bits(g, (nt, shape.Hp))
+    dy, dg = dataflow.combine_backward(dout, y, gates, plan, cfg)
+    # <dout, combine(y)> = <dy, y>: combine is linear in y
+    lhs = np.sum(f64(dout) * f64(dataflow.combine(y, gates, plan, cfg)))
+    assert lhs == np.sum(f64(dy) * f64(y))
+    # combine is linear in each gate: a unit step of g[t, k] changes
+    # <dout, out> by exactly dgates[t, k]
+    for t, k in [(0, 0), (1, K - 1), (nt - 1, 0), (nt // 2, K // 2)]:
+        g2 = gates.copy()
+        g2[t, k] += 1.0
+        rhs = np.sum(f64(dout) * f64(dataflow.combine(y, g2, plan, cfg)))
+        assert rhs - lhs == dg[t, k]
+
+
+def test_combine_backward_rounds_the_exact_product_once():
+    # gates with a full 24-bit significand: g * dout needs up to 32 bits, so
+    # rounding through fp32 first would differ from one rounding of the exact
+    # product for some entries (the test asserts it does here).  Every dy
+    # value must be the bf16 nearest to the exact product, ties to even.
+    from fractions import Fraction
+    shape = W.TINY.with_(S=64)
+    cfg, ids, _, plan = tiny_setup(shape, seed=2)
+    g = np.random.default_rng(4)
+    gates = g.random((shape.tokens, shape.K)).astype(np.float32)
+    dout = rand_bits(g, (shape.tokens, shape.Hp))
+    y = rand_bits(g, (shape.R * shape.SK, shape.Hp))
+    # planted pairs (gate bits, dout value) whose fp32 product sits exactly
+    # on a bf16 rounding midpoint while the exact product does not
+    planted = [(1063494377, 0.171875), (1055868370, -0.171875),
+               (1062663076, 2.265625), (1052535658, -2.234375)]
+    for i, (gb, dv) in enumerate(planted):
+        gates[5 + i, i % shape.K] = np.array(gb, np.uint32).view(np.float32)
+        dout[5 + i, 3 * i] = bf16.f64_to_bits(np.array(dv))
+    dy, _ = dataflow.combine_backward(dout, y, gates, plan, cfg)
+    route = plan.route.reshape(-1, shape.K)
+
+    def nearest_bf16(q):
+        # candidates: the two bf16 values around q (8 significant bits)
+        if q == 0:
+            return Fraction(0)
+        e = int(np.floor(np.log2(abs(float(q)))))
+        step = Fraction(2) ** (e - 7)
+        lo = (q // step) * step
+        hi = lo + step
+        if q - lo != hi - q:
+            return lo if q - lo < hi - q else hi
+        return lo if (lo / step) % 2 == 0 else hi
+
+    via_fp32_differs = 0
+    for t in range(shape.tokens):
+        for k in range(shape.K):
+            gk = Fraction(float(gates[t, k]))
+            for h in range(shape.Hp):
+                exact = gk * Fraction(float(f64(dout[t, h])))
+                want = nearest_bf16(exact)
+                assert Fraction(float(f64(dy[route[t, k], h]))) == want, (t, k, h)
+                p32 = Fraction(float(np.float32(gates[t, k]) * np.float32(f64(dout[t, h]))))
+                via_fp32_differs += nearest_bf16(p32) != want
+    assert via_fp32_differs >= len(planted)
+
+
+@pytest.mark.parametrize("mode,B", [(0, 2), (1, 1), (1, 0)])
+def test_dgrad_adjoint_of_grouped_gemm(mode, B):
+    shape = W.TINY.with_(H=32, Hp=16, mode=mode, B=B)
+    cfg, ids, _, plan = tiny_setup(shape, seed=9)
+    g = np.random.default_rng(13)
+    xp = int_bits(g, (shape.R * shape.SK, shape.H), -1, 1)
+    wh = int_bits(g, (shape.E, shape.H, shape.Hp), -1, 1)
+    wp = dataflow.prefetch(wh, plan, cfg)
+    dyb = int_bits(g, (shape.R * shape.SK, shape.Hp), -1, 1)
+    y = dataflow.grouped_gemm(xp, wh, wp, plan, cfg)
+    dx = dataflow.dgrad(dyb, wh, wp, plan, cfg)
+    assert np.sum(f64(dyb) * f64(y)) == np.sum(f64(dx) * f64(xp))
+    rows = np.arange(0, shape.R * shape.SK, 3)
+    assert np.array_equal(dataflow.dgrad_rows(rows, dyb, wh, wp, plan, cfg), dx[rows])
+
+
+def test_dgrad_closed_form_scaled_identity():
+    # W[e] = c_e * I: dxperm rows of segment j are c_j * dy rows exactly.
+    shape = W.TINY.with_(H=64, Hp=64)
+    cfg, ids, _, plan = tiny_setup(shape, seed=3)
+    g = np.random.default_rng(8)
+    c = 2.0 ** (np.arange(shape.E) - 3)
+    wh = bf16.f64_to_bits(c[:, None, None] * np.eye(64)[None])
+    wp = dataflow.prefetch(wh, plan, cfg)
+    dyb = rand_bits(g, (shape.R * shape.SK, shape.Hp))
+    dx = dataflow.dgrad(dyb, wh, wp, plan, cfg)
+    for r in range(shape.R):
+        for j in range(shape.E + shape.B):
+            lo, hi = plan.cu_seqlens[r, j], plan.cu_seqlens[r, j + 1]
+            e = j if j < shape.E else plan.slot_expert[r, j - shape.E]
+            rows = slice(r * shape.SK + lo, r * shape.SK + hi)
+            assert np.array_equal(f64(dx[rows]), c[e] * f64(dyb[rows]))
+
+
+@pytest.mark.parametrize("shape", [W.TINY, W.TINY.with_(B=1, mode=1),
+                                   W.TINY.with_(R=2, E=8, K=3, S=10, B=4)])
+def test_dispatch_backward_adjoint_and_round_trip(shape):
+    g = np.random.default_rng(17)
+    cfg, ids, _, plan = tiny_setup(shape, seed=1)
+    x = int_bits(g, (shape.tokens, shape.H))
+    dxp = int_bits(g, (shape.R * shape.SK, shape.H))
+    dx = dataflow.dispatch_backward(dxp, plan, cfg)
+    assert np.sum(f64(dxp) * f64(dataflow.dispatch(x, plan, cfg))) == np.sum(f64(dx) * f64(x))
+    # every route is valid here, so the K copies of x sum back to K * x
+    back = dataflow.dispatch_backward(dataflow.dispatch(x, plan, cfg), plan, cfg)
+    assert np.array_equal(f64(back), shape.K * f64(x))
