@@ -10,7 +10,10 @@ H=7168, H'=2048, B=E/R=48, bf16, Zipf-biased routing tuned to maxvio 1):
 All inputs are resident in HBM before timing starts.  W untimed warmup
 steps, then K timed steps bracketed by device synchronisation; every entry
 point is also bracketed by HIP events on the stream it runs on, giving each
-step's average duration.  Prints one JSON line.
+step's average duration.  After the timed steps the data backward of the
+layer (combine backward -> data-gradient GEMM -> dispatch backward) is timed
+the same way and reported beside the step ("data_backward"), outside
+`value`.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
                     [--sweep] [--no-cpu-baseline]
@@ -44,6 +47,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_bench_shape.txt")
 KERNEL_SOURCES = {"k_gemm<0>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<1>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_gemm<2>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_combine_bwd": "moe_expert_load_amd/csrc/copy.hip",
+                  "k_dispatch_bwd": "moe_expert_load_amd/csrc/copy.hip",
                   "k_dispatch": "moe_expert_load_amd/csrc/copy.hip",
                   "k_combine": "moe_expert_load_amd/csrc/copy.hip",
                   "k_prefetch": "moe_expert_load_amd/csrc/copy.hip",
@@ -159,6 +165,23 @@ class Path:
         self.gh = torch.zeros((s.E, s.H, s.Hp), dtype=torch.float32, device=dev)
         self.gp = torch.zeros((s.R * s.B, s.H, s.Hp), dtype=torch.float32, device=dev)
         self.ws = torch.empty(mx.moe_gemm_workspace_size(self.c), dtype=torch.uint8, device=dev)
+        # data backward
+        self.dout = W.randn_bf16((s.tokens, s.Hp), seed + 4, dev)
+        self.dy_b = torch.empty((s.R * s.SK, s.Hp), dtype=torch.bfloat16, device=dev)
+        self.dgates = torch.empty((s.tokens, s.K), dtype=torch.float32, device=dev)
+        self.dxperm = torch.empty((s.R * s.SK, s.H), dtype=torch.bfloat16, device=dev)
+        self.dx = torch.empty((s.tokens, s.H), dtype=torch.bfloat16, device=dev)
+
+    def backward_calls(self):
+        c, p = self.c, self.plan
+        return (
+            ("combine_bwd", lambda: mx.moe_combine_backward(c, p, self.dout, self.y, self.gates,
+                                                            self.dy_b, self.dgates)),
+            ("dgrad", lambda: mx.moe_grouped_gemm_dgrad(c, self.dy_b, self.w_home, self.w_pref,
+                                                        p.cu_seqlens, self.dxperm, 0,
+                                                        self.shape.R, self.ws)),
+            ("dispatch_bwd", lambda: mx.moe_dispatch_backward(c, p, self.dxperm, self.dx)),
+        )
 
     def calls(self):
         c, p = self.c, self.plan
@@ -174,8 +197,9 @@ class Path:
             ("reduce_grad", lambda: mx.moe_reduce_grad(c, p, self.gh, self.gp)),
         )
 
-    def run(self, steps, timed, only=None):
-        calls = [(n, f) for n, f in self.calls() if only is None or n in only]
+    def run(self, steps, timed, only=None, backward=False):
+        calls = [(n, f) for n, f in (self.backward_calls() if backward else self.calls())
+                 if only is None or n in only]
         ev = []
         for _ in range(steps):
             row = []
@@ -209,6 +233,11 @@ def work_units(shape, plan_views):
         "combine": ("bytes", float(T) * (2 * Hp * (K + 1) + 8 * K)),
         "wgrad": ("flops", 2.0 * H * Hp * rows),
         "reduce_grad": ("bytes", 8.0 * H * Hp * (n_slots + n_cons)),
+        # data backward: read dout and K y rows, write K dy rows, gates/routes
+        # in and gate gradients out; data-gradient GEMM; K rows in, one out
+        "combine_bwd": ("bytes", float(T) * (2 * Hp * (1 + 2 * K) + 12 * K)),
+        "dgrad": ("flops", 2.0 * H * Hp * rows),
+        "dispatch_bwd": ("bytes", float(T) * (2 * H * (K + 1) + 4 * K)),
     }, {"slots": n_slots, "experts_with_slots": n_cons}
 
 
@@ -251,7 +280,7 @@ def cpu_baseline(shape, ids, gates, path, budget_s=25.0):
     nseg = len(nz)
     t_gemm = t_conv * nseg + max(t_rows - 4 * t_conv, 0.0) / len(rows) * (s.R * s.SK)
     # combine: 2048 tokens from synthetic y rows
-    yrows = rng.integers(0, 2 ** 15, (len(toks) * s.K, s.Hp)).astype(np.uint16)
+    yrows = bf16.f64_to_bits(rng.standard_normal((len(toks) * s.K, s.Hp)))
     t0 = time.perf_counter()
     acc = np.zeros((len(toks), s.Hp))
     for k in range(s.K):
@@ -320,6 +349,41 @@ def measure(path, steps, warmup):
     ms = {n: float(np.mean(v)) for n, v in per.items() if v}
     span = ev[0][0][1].elapsed_time(ev[-1][-1][2])
     return ms, span / steps, wall / steps * 1e3
+
+
+def measure_backward(path, steps, warmup):
+    path.run(warmup, timed=False, backward=True)
+    torch.cuda.synchronize()
+    ev = path.run(steps, timed=True, backward=True)
+    torch.cuda.synchronize()
+    per = {}
+    for row in ev:
+        for name, a, b in row:
+            per.setdefault(name, []).append(a.elapsed_time(b))
+    return {n: float(np.mean(v)) for n, v in per.items()}
+
+
+def plan_latency(shape, target, runs=20):
+    """Plan µs (all four planner launches) at one routing of one shape."""
+    ids, _, _, mv = W.routing_zipf(shape, target)
+    c = mx.make_cfg(shape.R, shape.S, shape.E, shape.K, shape.H, shape.Hp, shape.B, shape.mode)
+    plan = mx.Plan(c)
+    ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    for _ in range(3):
+        mx.moe_plan_run(c, ids_t, plan)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(runs):
+        a.record()
+        mx.moe_plan_run(c, ids_t, plan)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    st = plan.views()["status"].cpu().numpy()
+    return {"maxvio": mv, "plan_us_median": float(np.median(ts)), "plan_us_min": float(min(ts)),
+            "fills": int(st[0]), "moves": int(st[1]), "status": int(st[2])}
 
 
 def main():
@@ -432,6 +496,28 @@ def main():
         "roofline": roofline,
         "rooflines": roof,
     }
+    log("plan latency at the Large-E shape")
+    line["plan_large_e"] = {"workload": "Large-E: R=64, S=4096, E=896, K=16, B=14 (plan only)",
+                            "maxvio_1": plan_latency(W.LARGE_E, 1.0),
+                            "maxvio_10": plan_latency(W.LARGE_E, 10.0)}
+    log("data backward")
+    bms = measure_backward(path, max(3, args.steps // 2), 1)
+    bwd = []
+    for name, kern in (("combine_bwd", "k_combine_bwd"), ("dgrad", "k_gemm<2>"),
+                       ("dispatch_bwd", "k_dispatch_bwd")):
+        kind, amount = units[name]
+        t = bms[name] * 1e-3
+        if kind == "flops":
+            ach = amount / t / 1e12
+            bwd.append({"step": name, "kernel": kern, "bound": "mfma", "achieved": ach,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": ach / BF16_PEAK_TFLOPS, "ms": bms[name]})
+        else:
+            ach = amount / t / 1e9
+            bwd.append({"step": name, "kernel": kern, "bound": "hbm", "achieved": ach,
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                        "ms": bms[name]})
+    line["data_backward"] = bwd
     if args.sweep:
         sweep = {}
         for t in W.MAXVIO_SWEEP["bench"]:

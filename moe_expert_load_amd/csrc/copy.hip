@@ -87,11 +87,10 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
 #define MOONEP_COMBINE_KB 8
 #endif
 template <int CU, int KB, bool kUnit>
-__global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
-                                                 const float* __restrict__ gates,
-                                                 const int32_t* __restrict__ route,
-                                                 u32x4* __restrict__ out, int ntok, int K,
-                                                 int hv) {
+__device__ __forceinline__ void combine_rows(const u32x4* __restrict__ y,
+                                             const float* __restrict__ gates,
+                                             const int32_t* __restrict__ route,
+                                             u32x4* __restrict__ out, int ntok, int K, int hv) {
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= ntok) return;
   const int lane = lane_id();
@@ -142,6 +141,24 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
       }
     }
   }
+}
+
+
+template <int CU, int KB>
+__global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ y,
+                                                 const float* __restrict__ gates,
+                                                 const int32_t* __restrict__ route,
+                                                 u32x4* __restrict__ out, int ntok, int K,
+                                                 int hv) {
+  combine_rows<CU, KB, false>(y, gates, route, out, ntok, K, hv);
+}
+
+template <int CU, int KB>
+__global__ __launch_bounds__(256) void k_dispatch_bwd(const u32x4* __restrict__ dxperm,
+                                                      const int32_t* __restrict__ route,
+                                                      u32x4* __restrict__ dx, int ntok, int K,
+                                                      int hv) {
+  combine_rows<CU, KB, true>(dxperm, nullptr, route, dx, ntok, K, hv);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,7 +349,7 @@ extern "C" int moe_combine(const moe_cfg* cfg, const moe_plan* plan, const moe_b
   const u32x4* ys = reinterpret_cast<const u32x4*>(y);
   u32x4* od = reinterpret_cast<u32x4*>(out);
 #define MOE_COMBINE(N)                                                                          \
-  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB, false>), grid, block, 0, stream, ys, gates, \
+  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB>), grid, block, 0, stream, ys, gates,        \
                      plan->route, od, ntok, cfg->K, hv)
   if (cu <= 1) MOE_COMBINE(1);
   else if (cu <= 2) MOE_COMBINE(2);
@@ -378,8 +395,8 @@ extern "C" int moe_dispatch_backward(const moe_cfg* cfg, const moe_plan* plan,
   const u32x4* xs = reinterpret_cast<const u32x4*>(dxperm);
   u32x4* od = reinterpret_cast<u32x4*>(dx);
 #define MOE_UNDISPATCH(N)                                                                   \
-  hipLaunchKernelGGL((k_combine<N, MOONEP_COMBINE_KB, true>), grid, block, 0, stream, xs,    \
-                     (const float*)nullptr, plan->route, od, ntok, cfg->K, hv)
+  hipLaunchKernelGGL((k_dispatch_bwd<N, MOONEP_COMBINE_KB>), grid, block, 0, stream, xs,      \
+                     plan->route, od, ntok, cfg->K, hv)
   if (cu <= 1) MOE_UNDISPATCH(1);
   else if (cu <= 2) MOE_UNDISPATCH(2);
   else MOE_UNDISPATCH(4);

@@ -1,29 +1,36 @@
-// Grouped GEMM over the [E+B, H, H'] weight view, and its fp32 weight
-// gradient, on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+// Grouped GEMM over the [E+B, H, H'] weight view, its fp32 weight gradient
+// and its data gradient, on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
 //
 // Sources: "Moonshot AI 开源 MoonEP", 核心思想 (the grouped GEMM addresses
 // experts only by row index of one [E+B, H, H'] tensor; cu_seqlens[E+B]
 // picks the active rows; gradients mirror the layout in fp32 with rows
 // [E, E+B) in a separate reduce buffer); "Kimi K3 模型结构（8）", rank 内部
 // (per-expert row counts stay skewed inside a rank, so work is handed out by
-// a load-aware scheduler rather than in a fixed order).
+// a load-aware scheduler rather than in a fixed order); "大规模 LLM 训练系统
+// 研究账本" §9.5 (the backward runs over the rows dispatch laid out).
 //
 // Structure:
-//   k_sched_*   one workgroup turns cu_seqlens into a flat work list on the
+//   k_sched<MODE> one workgroup turns cu_seqlens into a flat work list on the
 //               device (no host round trip: the grid never depends on it);
 //   k_gemm<MODE> a persistent grid, one 256-thread workgroup per CU, pulls
 //               256x256 output tiles from that list.  Consecutive work items
 //               go to the 32 workgroups of one XCD (blockIdx % 8 picks the
-//               XCD), so the A panel and the weight panels of neighbouring
-//               tiles are shared in that XCD's L2.
+//               XCD); inside a segment of row tiles the forward and the data
+//               gradient go column tile by column tile, so the CUs of one
+//               XCD share each weight panel across all of the segment's row
+//               tiles in that XCD's L2.
+//   MODE 0: y = xperm_seg @ W (forward); MODE 1: G = xperm_seg^T @ dy_seg
+//   (weight gradient, fp32); MODE 2: dxperm_seg = dy_seg @ W^T (data
+//   gradient, over the forward's work list).
 // Tile: BM = BN = 256, BK = 32; 4 waves in a 2x2 grid, each 128x128 =
 // 4x4 MFMA blocks of 32x32 with fp32 accumulators (256 AGPRs per wave).
 // Operands go from global memory straight into LDS (buffer_load ... lds,
 // range-checked so ragged tails read zeros) through a 4-stage ring of
 // separate LDS arrays, with 16-byte-chunk XOR swizzles that make every LDS
 // read conflict free.  An operand whose k index is contiguous (the permuted
-// activations in the forward) is read with ds_read_b128; an operand whose
-// k index is strided (the weight [H][H'], dy, and x^T in the weight
+// activations in the forward; dy and the weight rows in the data gradient)
+// is a "row tile" read with ds_read_b128; an operand whose k index is
+// strided (the weight [H][H'] in the forward; x^T and dy in the weight
 // gradient) is stored as loaded, [k][col], and read with the transposing
 // ds_read_b64_tr_b16, which returns 4 consecutive k per lane.  Fragment
 // reads of the next 16-deep substep are interleaved with the MFMAs of the
@@ -44,12 +51,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BM = 256, BN = 256;
+
+// Work order of the forward: 0 = row tile major (each row tile's column
+// tiles adjacent), 1 = column tile major inside a segment.
+#ifndef MOONEP_FWD_NMAJOR
+#define MOONEP_FWD_NMAJOR 1
+#endif
 constexpr int kGemmThreads = 256;
 
 enum { MODE_FWD = 0, MODE_WGRAD = 1, MODE_DGRAD = 2 };
 
 struct WorkItem {
   int32_t r, j, row0, rows;  // rank, weight row, first xperm row (absolute), row count
+  int32_t first, cnt;        // row-tile lists: the segment's first item and its item count
 };
 
 struct GemmArgs {
@@ -212,6 +226,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   // Operand tiles: a "row tile" holds k-contiguous rows (forward A, and
   // both operands of the data gradient), a "col tile" k-strided rows.
   constexpr bool kRowA = MODE != MODE_WGRAD, kRowB = MODE == MODE_DGRAD;
+  constexpr bool kNMajor = MODE == MODE_DGRAD || (MODE == MODE_FWD && MOONEP_FWD_NMAJOR);
   const int H = g.H, Hp = g.Hp;
   const int ntm = MODE == MODE_WGRAD ? (H + BM - 1) / BM : 1;
   const int NOUT = MODE == MODE_DGRAD ? H : Hp;          // output columns
@@ -244,10 +259,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   for (int64_t q = 0;; ++q) {
     const int64_t w = q * G + int64_t(xcd) * per + local;
     if (w >= total) break;
-    const int64_t item = w / (ntm * ntn);
-    const int rest = (int)(w % (ntm * ntn));
-    const int tm = rest / ntn, tn = rest % ntn;
-    const WorkItem it = g.items[item];
+    int tm, tn;
+    WorkItem it;
+    if (kNMajor) {
+      // Column-tile major inside a segment: the segment of row tiles
+      // [first, first + cnt) owns work [first*ntn, (first + cnt)*ntn), and
+      // w there is (tn, row tile) = divmod(w - first*ntn, cnt).  Neighbouring
+      // work shares one weight panel across the segment's row tiles.
+      const WorkItem h = g.items[w / ntn];
+      const int loc = (int)(w - int64_t(h.first) * ntn);
+      tm = 0;
+      tn = loc / h.cnt;
+      it = g.items[h.first + loc % h.cnt];
+    } else {
+      const int64_t item = w / (ntm * ntn);
+      const int rest = (int)(w % (ntm * ntn));
+      tm = rest / ntn;
+      tn = rest % ntn;
+      it = g.items[item];
+    }
     const int n0 = tn * BN, m0 = tm * BM;
     const int KD = MODE == MODE_FWD ? H : MODE == MODE_DGRAD ? Hp : it.rows;
     // k-tiles, rounded up to whole passes over the stages: tiles past the
@@ -617,6 +647,8 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
           w.row0 = r * s.SK + lo;
           w.rows = len;
         }
+        w.first = base;
+        w.cnt = cnt;
         s.items[at] = w;
       }
     }
