@@ -171,6 +171,8 @@ class Path:
         self.dgates = torch.empty((s.tokens, s.K), dtype=torch.float32, device=dev)
         self.dxperm = torch.empty((s.R * s.SK, s.H), dtype=torch.bfloat16, device=dev)
         self.dx = torch.empty((s.tokens, s.H), dtype=torch.bfloat16, device=dev)
+        # dedup dispatch
+        self.route_enc = torch.empty(s.tokens * s.K, dtype=torch.int32, device=dev)
 
     def backward_calls(self):
         c, p = self.c, self.plan
@@ -351,6 +353,47 @@ def measure(path, steps, warmup):
     return ms, span / steps, wall / steps * 1e3
 
 
+def measure_dedup(path, steps):
+    """Route encoding and the two-phase dispatch, beside the plain dispatch."""
+    s, c, p = path.shape, path.c, path.plan
+    enc_f = lambda: mx.moe_route_encode(c, p, path.route_enc)
+    disp_f = lambda: mx.moe_dispatch_dedup(c, path.route_enc, path.x, path.xperm)
+    for f in (enc_f, disp_f):
+        f()
+    torch.cuda.synchronize()
+    ts = {"route_encode": [], "dispatch_dedup": []}
+    for _ in range(steps):
+        for name, f in (("route_encode", enc_f), ("dispatch_dedup", disp_f)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts[name].append(a.elapsed_time(b))
+    enc = path.route_enc.view(-1, s.K).cpu().numpy().astype(np.int64)
+    route = p.views()["route"].cpu().numpy().reshape(-1, s.K).astype(np.int64)
+    src = (np.arange(s.tokens) // s.S)[:, None]
+    off_rank = (route // s.SK) != src
+    sent = enc >= 0
+    n_slots = route.size
+    d_total = int(sent.sum())
+    row = 2.0 * s.H
+    ms_d = float(np.mean(ts["dispatch_dedup"]))
+    algo = s.tokens * row + d_total * row + (n_slots - d_total) * 2 * row + 4.0 * n_slots
+    return {
+        "route_encode_us": float(np.mean(ts["route_encode"])) * 1e3,
+        "dispatch_dedup_ms": ms_d,
+        "dispatch_dedup_GBps": algo / (ms_d * 1e-3) / 1e9,
+        "payload_rows": {"plain": int(n_slots), "dedup": d_total},
+        "cross_rank_payload_GB": {"plain": float(off_rank.sum()) * row / 1e9,
+                                  "dedup": float((off_rank & sent).sum()) * row / 1e9},
+        "note": "on one GPU the send pass writes one row per (token, rank) and the receive "
+                "pass copies the repeats locally; cross_rank_payload_GB is what would cross "
+                "xGMI links with one rank per GPU",
+    }
+
+
 def measure_backward(path, steps, warmup):
     path.run(warmup, timed=False, backward=True)
     torch.cuda.synchronize()
@@ -518,6 +561,8 @@ def main():
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                         "ms": bms[name]})
     line["data_backward"] = bwd
+    log("dedup dispatch")
+    line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
     if args.sweep:
         sweep = {}
         for t in W.MAXVIO_SWEEP["bench"]:

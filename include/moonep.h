@@ -18,6 +18,11 @@
  *   moe_grouped_gemm_dgrad  dxperm = dy @ W^T over the same rows
  *   moe_dispatch_backward   sum each token's K permuted gradient rows
  *
+ * and the deduplicated dispatch:
+ *
+ *   moe_route_encode     route map with repeats on a rank as -(row)-1
+ *   moe_dispatch_dedup   payload once per (token, rank), then local copies
+ *
  * Sources: "Kimi K3 模型结构（8）：训练并行，MoonEP 与四类等待" (blog.javazero.top),
  * "Moonshot AI 开源 MoonEP" (feinterview), "MoonEP : l'équilibrage parfait"
  * (mkdocs.reaper.mx), "大规模 LLM 训练系统研究账本" (llm-atlas); each entry
@@ -266,6 +271,30 @@ int moe_grouped_gemm_dgrad(const moe_cfg *cfg, const moe_bf16 *dy,
 int moe_dispatch_backward(const moe_cfg *cfg, const moe_plan *plan,
                           const moe_bf16 *dxperm, moe_bf16 *dx,
                           hipStream_t stream);
+
+/*
+ * Dedup encoding of the route map ("Kimi K3 模型结构（8）", 在线规划、零拷贝、
+ * 静态 shape: a route entry holds its write position on the destination rank;
+ * an entry whose rank already appeared among the same token's earlier
+ * entries holds -(position) - 1 instead, so the sender skips its payload).
+ * With q = route[t*K + k] and rank d = q / (S*K), for k ascending:
+ *   route_enc[t*K + k] = q            if no k' < k of token t has rank d
+ *                      = -q - 1       otherwise
+ *                      = INT32_MIN    if q < 0 (no plan)
+ * route_enc [R*S][K] int32 (caller-allocated, device).
+ */
+int moe_route_encode(const moe_cfg *cfg, const moe_plan *plan, int32_t *route_enc,
+                     hipStream_t stream);
+
+/*
+ * Dispatch driven by route_enc (same source): a send pass writes each
+ * token's row once per destination rank (entries >= 0); a receive pass then
+ * copies, on each rank, the row that arrived for the token into every row
+ * -(e) - 1 of that token on that rank.  The result equals moe_dispatch's
+ * bit for bit.  x [R*S][H], xperm [R][S*K][H] bf16.
+ */
+int moe_dispatch_dedup(const moe_cfg *cfg, const int32_t *route_enc,
+                       const moe_bf16 *x, moe_bf16 *xperm, hipStream_t stream);
 
 /* Host only.  Static text for a MOE_* return code. */
 const char *moe_strerror(int code);

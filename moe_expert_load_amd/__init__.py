@@ -22,7 +22,8 @@ ENTRY_POINTS = ("moe_plan_sizes", "moe_plan_run", "moe_prefetch_weight",
                 "moe_dispatch", "moe_gemm_workspace_size", "moe_grouped_gemm",
                 "moe_combine", "moe_grouped_gemm_wgrad", "moe_reduce_grad",
                 "moe_combine_backward", "moe_grouped_gemm_dgrad",
-                "moe_dispatch_backward", "moe_strerror")
+                "moe_dispatch_backward", "moe_route_encode", "moe_dispatch_dedup",
+                "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -71,6 +72,8 @@ def load(path=None):
         "moe_combine_backward": [C, PL, P, P, P, P, P, P],
         "moe_grouped_gemm_dgrad": [C, P, P, P, P, P, I32, I32, P, P],
         "moe_dispatch_backward": [C, PL, P, P, P],
+        "moe_route_encode": [C, PL, P, P],
+        "moe_dispatch_dedup": [C, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -263,6 +266,22 @@ def moe_dispatch_backward(cfg, plan, dxperm, dx, stream=None):
     o = _ptr(dx, torch.bfloat16, ntok * cfg.H, "dx")
     _check(load().moe_dispatch_backward(ctypes.byref(cfg), plan.c, a, o, _stream(stream)),
            "moe_dispatch_backward")
+
+
+def moe_route_encode(cfg, plan, route_enc, stream=None):
+    e = _ptr(route_enc, torch.int32, cfg.R * cfg.S * cfg.K, "route_enc")
+    _check(load().moe_route_encode(ctypes.byref(cfg), plan.c, e, _stream(stream)),
+           "moe_route_encode")
+
+
+def moe_dispatch_dedup(cfg, route_enc, x, xperm, stream=None):
+    ntok = cfg.R * cfg.S
+    args = (ctypes.byref(cfg),
+            _ptr(route_enc, torch.int32, ntok * cfg.K, "route_enc"),
+            _ptr(x, torch.bfloat16, ntok * cfg.H, "x"),
+            _ptr(xperm, torch.bfloat16, ntok * cfg.K * cfg.H, "xperm"),
+            _stream(stream))
+    _check(load().moe_dispatch_dedup(*args), "moe_dispatch_dedup")
 
 
 def moe_reduce_grad(cfg, plan, grad_home, grad_pref, stream=None):

@@ -77,6 +77,89 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
+// Dedup encoding of the route map and the two-phase dispatch it drives
+// ("Kimi K3 模型结构（8）", 在线规划、零拷贝、静态 shape: a route whose
+// destination rank already appeared among the token's earlier routes holds
+// -(position) - 1 and carries no payload; the receiver copies the row it
+// got once).  Positions are rows of the stacked [R*S*K] buffer.
+// ---------------------------------------------------------------------------
+constexpr int32_t kNoDest = INT32_MIN;
+
+__global__ __launch_bounds__(256) void k_route_encode(const int32_t* __restrict__ route,
+                                                      int32_t* __restrict__ enc, int ntok, int K,
+                                                      int SK) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= ntok) return;
+  const int32_t* r = route + int64_t(t) * K;
+  int32_t* o = enc + int64_t(t) * K;
+  for (int k = 0; k < K; ++k) {
+    const int q = r[k];
+    if (q < 0) { o[k] = kNoDest; continue; }
+    const int d = q / SK;
+    bool seen = false;
+    for (int k2 = 0; k2 < k; ++k2) seen |= r[k2] >= 0 && r[k2] / SK == d;
+    o[k] = seen ? -q - 1 : q;
+  }
+}
+
+// send: one wave per token; its row is read once and written once per
+// destination rank (entries >= 0).
+template <int DU>
+__global__ __launch_bounds__(256) void k_dispatch_send(const u32x4* __restrict__ x,
+                                                       u32x4* __restrict__ xperm,
+                                                       const int32_t* __restrict__ enc, int ntok,
+                                                       int K, int hv) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= ntok) return;
+  const int lane = lane_id();
+  const int mine = lane < K ? enc[int64_t(t) * K + lane] : -1;
+  const u32x4* src = x + int64_t(t) * hv;
+  for (int c0 = 0; c0 < hv; c0 += kWave * DU) {
+    u32x4 v[DU];
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < hv) v[u] = src[c];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int dst = __shfl(mine, k, kWave);
+      if (dst < 0) continue;
+      u32x4* d = xperm + int64_t(dst) * hv;
+#pragma unroll
+      for (int u = 0; u < DU; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < hv) d[c] = v[u];
+      }
+    }
+  }
+}
+
+// receive side: one wave per token; every entry -(q) - 1 copies the row that
+// arrived on q's rank for this token (that rank's entry >= 0) into row q.
+__global__ __launch_bounds__(256) void k_dispatch_expand(u32x4* __restrict__ xperm,
+                                                         const int32_t* __restrict__ enc,
+                                                         int ntok, int K, int SK, int hv) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= ntok) return;
+  const int lane = lane_id();
+  const int mine = lane < K ? enc[int64_t(t) * K + lane] : kNoDest;
+  for (int k = 0; k < K; ++k) {
+    const int e = __shfl(mine, k, kWave);
+    if (e >= 0 || e == kNoDest) continue;
+    const int q = -(e + 1);
+    int src = -1;
+    for (int k2 = 0; k2 < K && src < 0; ++k2) {
+      const int f = __shfl(mine, k2, kWave);
+      if (f >= 0 && f / SK == q / SK) src = f;
+    }
+    if (src < 0) continue;                      // never: the rank's first entry is >= 0
+    const u32x4* s = xperm + int64_t(src) * hv;
+    u32x4* d = xperm + int64_t(q) * hv;
+    for (int c = lane; c < hv; c += kWave) d[c] = s[c];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine: one wave per token; out = sum_k g_k * y[route_k] in fp32, k
 // ascending, rounded once to bf16.  The rows of KB routes are loaded before
 // any of them is accumulated, so KB * CU 16-byte loads per lane are in
@@ -333,6 +416,44 @@ extern "C" int moe_dispatch(const moe_cfg* cfg, const moe_plan* plan, const moe_
   else if (du <= 14) MOE_DISPATCH(14);
   else MOE_DISPATCH(16);
 #undef MOE_DISPATCH
+  return hip_status();
+}
+
+extern "C" int moe_route_encode(const moe_cfg* cfg, const moe_plan* plan, int32_t* route_enc,
+                                hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  const int ntok = cfg->R * cfg->S;
+  if (ntok == 0) return MOE_OK;
+  if (!plan || !plan->route || !route_enc) return MOE_EINVAL;
+  hipLaunchKernelGGL(k_route_encode, dim3((ntok + 255) / 256), dim3(256), 0, stream, plan->route,
+                     route_enc, ntok, cfg->K, cfg->S * cfg->K);
+  return hip_status();
+}
+
+extern "C" int moe_dispatch_dedup(const moe_cfg* cfg, const int32_t* route_enc, const moe_bf16* x,
+                                  moe_bf16* xperm, hipStream_t stream) {
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  const int ntok = cfg->R * cfg->S;
+  if (ntok == 0) return MOE_OK;
+  if (!route_enc || !x || !xperm) return MOE_EINVAL;
+  const int hv = cfg->H / 8;
+  const int du = (hv + kWave - 1) / kWave;
+  const dim3 grid((ntok + 3) / 4), block(256);
+  const u32x4* xs = reinterpret_cast<const u32x4*>(x);
+  u32x4* xd = reinterpret_cast<u32x4*>(xperm);
+#define MOE_SEND(N) \
+  hipLaunchKernelGGL(k_dispatch_send<N>, grid, block, 0, stream, xs, xd, route_enc, ntok, cfg->K, hv)
+  if (du <= 1) MOE_SEND(1);
+  else if (du <= 2) MOE_SEND(2);
+  else if (du <= 4) MOE_SEND(4);
+  else if (du <= 8) MOE_SEND(8);
+  else if (du <= 14) MOE_SEND(14);
+  else MOE_SEND(16);
+#undef MOE_SEND
+  hipLaunchKernelGGL(k_dispatch_expand, grid, block, 0, stream, xd, route_enc, ntok, cfg->K,
+                     cfg->S * cfg->K, hv);
   return hip_status();
 }
 

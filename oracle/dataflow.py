@@ -280,3 +280,61 @@ def dispatch_backward(dxperm_bits, plan, cfg):
         ok = route[:, k] >= 0
         acc[ok] += bf16.bits_to_f64(x[route[ok, k]])
     return bf16.f64_to_bits(acc)
+
+
+NO_DEST = -(2 ** 31)        # encoded route of a slot that has no destination
+
+
+def route_encode(plan, cfg):
+    """Dedup encoding of the route map.
+
+    [K3-blog] "在线规划、零拷贝、静态 shape": each route entry holds its write
+    position on the destination rank; an entry whose destination rank already
+    appeared among the same token's earlier entries holds -(position) - 1,
+    so the sender skips its payload and the receiver copies the row it got
+    once.  Positions here are rows of the stacked [R*S*K] buffer (rank =
+    row // (S*K)); k is scanned in ascending order; a slot without a route
+    (-1) becomes NO_DEST.
+    """
+    K, SK = cfg.K, cfg.SK
+    route = plan.route.reshape(-1, K).astype(np.int64)
+    enc = np.empty_like(route)
+    for t in range(route.shape[0]):
+        seen = set()
+        for k in range(K):
+            q = int(route[t, k])
+            if q < 0:
+                enc[t, k] = NO_DEST
+                continue
+            d = q // SK
+            enc[t, k] = q if d not in seen else -q - 1
+            seen.add(d)
+    return enc.reshape(-1).astype(np.int32)
+
+
+def dispatch_dedup(x_bits, enc, cfg):
+    """Two-phase dispatch driven by the encoded route.
+
+    Send: token t's row goes once to each destination rank (entries >= 0).
+    Receive: an entry -(q) - 1 copies, on its rank, the row that arrived for
+    the same token (the entry >= 0 of that rank) into row q.  [K3-blog]
+    "在线规划、零拷贝、静态 shape".  Returns the [R*S*K, H] permuted buffer.
+    """
+    K, SK = cfg.K, cfg.SK
+    enc = np.asarray(enc, np.int64).reshape(-1, K)
+    out = np.zeros((cfg.R * SK, cfg.H), np.uint16)
+    for t in range(enc.shape[0]):                 # send
+        for k in range(K):
+            if enc[t, k] >= 0:
+                out[enc[t, k]] = x_bits[t]
+    for t in range(enc.shape[0]):                 # receive-side local copies
+        first = {}
+        for k in range(K):
+            if enc[t, k] >= 0:
+                first.setdefault(int(enc[t, k]) // SK, int(enc[t, k]))
+        for k in range(K):
+            e = int(enc[t, k])
+            if e < 0 and e != NO_DEST:
+                q = -e - 1
+                out[q] = out[first[q // SK]]
+    return out

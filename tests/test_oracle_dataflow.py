@@ -293,3 +293,52 @@ def test_dispatch_backward_adjoint_and_round_trip(shape):
     # every route is valid here, so the K copies of x sum back to K * x
     back = dataflow.dispatch_backward(dataflow.dispatch(x, plan, cfg), plan, cfg)
     assert np.array_equal(f64(back), shape.K * f64(x))
+
+
+# ---------------------------------------------------------------------------
+# Dedup encoding ([K3-blog] 在线规划、零拷贝、静态 shape).  Pinned against the
+# plain route map and the pinned plain dispatch, not against itself.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,kind", [(W.TINY, "uniform"), (W.TINY, "hot"),
+                                        (W.TINY.with_(R=2, E=8, K=3, S=10, B=4), "uniform"),
+                                        (W.SKEWED.with_(S=64, H=16, Hp=16), "theorem2")])
+def test_route_encode_invariants_and_dedup_dispatch(shape, kind):
+    cfg = cfg_of(shape)
+    if kind == "hot":
+        ids = W.routing_hot(shape)
+    elif kind == "theorem2":
+        ids = W.routing_theorem2(shape)
+    else:
+        ids, _ = W.routing_uniform(shape, salt=4)
+    plan = make_plan(ids, cfg)
+    enc = dataflow.route_encode(plan, cfg).reshape(-1, shape.K)
+    route = plan.route.reshape(-1, shape.K)
+    SK = shape.SK
+    # decoding recovers the route; one non-negative entry per distinct
+    # destination rank of the token, and it is the first one in k order
+    dec = np.where(enc >= 0, enc, -enc.astype(np.int64) - 1)
+    assert np.array_equal(dec, route)
+    for t in range(route.shape[0]):
+        ranks = route[t] // SK
+        firsts = [k for k in range(shape.K) if ranks[k] not in ranks[:k]]
+        assert sorted(np.nonzero(enc[t] >= 0)[0].tolist()) == firsts
+    # the two-phase dispatch gives exactly the plain dispatch
+    g = np.random.default_rng(6)
+    x = rand_bits(g, (shape.tokens, shape.H))
+    assert np.array_equal(dataflow.dispatch_dedup(x, enc, cfg), dataflow.dispatch(x, plan, cfg))
+
+
+def test_route_encode_page_illustration():
+    # [K3-blog]: a token whose six routes land on three ranks sends its row
+    # three times; the repeats carry -(position) - 1.  Rows of rank d are
+    # [d*S*K, (d+1)*S*K); the six routes hit ranks 0, 0, 1, 2, 2, 1.
+    from types import SimpleNamespace
+    shape = W.TINY.with_(R=4, E=8, K=6, S=2, B=2)
+    cfg = cfg_of(shape)
+    SK = shape.SK
+    route = np.array([[0, 1, SK, 2 * SK, 2 * SK + 1, SK + 1],
+                      [2, 3 * SK, 3 * SK + 1, 3 * SK + 2, 3, SK + 2]] * 4, np.int32).reshape(-1)
+    enc = dataflow.route_encode(SimpleNamespace(route=route), cfg).reshape(-1, shape.K)
+    assert enc[0].tolist() == [0, -2, SK, 2 * SK, -(2 * SK + 1) - 1, -(SK + 1) - 1]
+    assert enc[1].tolist() == [2, 3 * SK, -(3 * SK + 1) - 1, -(3 * SK + 2) - 1, -4, SK + 2]
+    assert int((enc[0] >= 0).sum()) == 3
