@@ -287,6 +287,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       rp_off[h][s] = (wm * 128 + row) * 128 + ((kc ^ ((row >> 1) & 7)) << 4);
     }
 
+  // The work list is read-only here and every index is wave-uniform: read it
+  // through the constant address space (scalar loads, counted by lgkmcnt),
+  // so no wave has to wait for its vector-memory queue to fetch its next item.
+  typedef __attribute__((address_space(4))) const WorkItem const_item;
+  const const_item* items = (const const_item*)g.items;
+  auto item_at = [&](int64_t i) {
+    WorkItem v;
+    v.r = items[i].r;
+    v.j = items[i].j;
+    v.row0 = items[i].row0;
+    v.rows = items[i].rows;
+    v.first = items[i].first;
+    v.cnt = items[i].cnt;
+    return v;
+  };
   for (int64_t q = 0;; ++q) {
     const int64_t w = q * G + int64_t(xcd) * per + local;
     if (w >= total) break;
@@ -297,17 +312,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // [first, first + cnt) owns work [first*ntn, (first + cnt)*ntn), and
       // w there is (tn, row tile) = divmod(w - first*ntn, cnt).  Neighbouring
       // work shares one weight panel across the segment's row tiles.
-      const WorkItem h = g.items[w / ntn];
+      const WorkItem h = item_at(w / ntn);
       const int loc = (int)(w - int64_t(h.first) * ntn);
       tm = 0;
       tn = loc / h.cnt;
-      it = g.items[h.first + loc % h.cnt];
+      it = item_at(h.first + loc % h.cnt);
     } else {
       const int64_t item = w / (ntm * ntn);
       const int rest = (int)(w % (ntm * ntn));
       tm = rest / ntn;
       tn = rest % ntn;
-      it = g.items[item];
+      it = item_at(item);
     }
     const int n0 = tn * BN, m0 = tm * BM;
     const int KD = MODE == MODE_FWD ? H : MODE == MODE_DGRAD ? Hp : it.rows;
