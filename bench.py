@@ -37,6 +37,9 @@ METRIC = "plan µs + dispatch/combine GB/s + grouped-GEMM TFLOP/s @S8192 E384 K8
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 STEPS = ("plan", "prefetch", "dispatch", "gemm", "combine", "wgrad", "reduce_grad")
+# The step plans with the largest-remaining-first donor policy (the pages'
+# planner is a near-optimal heuristic); both policies are reported.
+PLAN_POLICY = mx.PLAN_LARGEST_FIRST
 
 
 def log(*a):
@@ -188,7 +191,7 @@ class Path:
     def calls(self):
         c, p = self.c, self.plan
         return (
-            ("plan", lambda: mx.moe_plan_run(c, self.ids, p)),
+            ("plan", lambda: mx.moe_plan_run_policy(c, self.ids, p, PLAN_POLICY)),
             ("prefetch", lambda: mx.moe_prefetch_weight(c, p, self.w_home, self.w_pref)),
             ("dispatch", lambda: mx.moe_dispatch(c, p, self.x, self.xperm)),
             ("gemm", lambda: mx.moe_grouped_gemm(c, self.xperm, self.w_home, self.w_pref,
@@ -247,13 +250,13 @@ def cpu_baseline(shape, ids, gates, path, budget_s=25.0):
     """The oracle on the host cores, on a bounded sample, scaled to a step."""
     from threadpoolctl import threadpool_info
     from oracle import bf16, dataflow
-    from oracle.plan import Cfg, make_plan
+    from oracle.plan import POLICY_LARGEST, Cfg, make_plan
 
     s = shape
     oc = Cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     t0 = time.perf_counter()
-    ref = make_plan(ids, oc)
+    ref = make_plan(ids, oc, POLICY_LARGEST if PLAN_POLICY == mx.PLAN_LARGEST_FIRST else 0)
     t_plan = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     # dispatch: 2048 tokens, their K rows (the oracle's fancy-index bit copy)
@@ -406,27 +409,31 @@ def measure_backward(path, steps, warmup):
     return {n: float(np.mean(v)) for n, v in per.items()}
 
 
-def plan_latency(shape, target, runs=20):
+def plan_latency(shape, target, runs=20, policy=PLAN_POLICY, ids=None):
     """Plan µs (all four planner launches) at one routing of one shape."""
-    ids, _, _, mv = W.routing_zipf(shape, target)
+    mv = None
+    if ids is None:
+        ids, _, _, mv = W.routing_zipf(shape, target)
     c = mx.make_cfg(shape.R, shape.S, shape.E, shape.K, shape.H, shape.Hp, shape.B, shape.mode)
     plan = mx.Plan(c)
     ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     for _ in range(3):
-        mx.moe_plan_run(c, ids_t, plan)
+        mx.moe_plan_run_policy(c, ids_t, plan, policy)
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     ts = []
     for _ in range(runs):
         a.record()
-        mx.moe_plan_run(c, ids_t, plan)
+        mx.moe_plan_run_policy(c, ids_t, plan, policy)
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b) * 1e3)
-    st = plan.views()["status"].cpu().numpy()
+    v = plan.views()
+    st = v["status"].cpu().numpy()
     return {"maxvio": mv, "plan_us_median": float(np.median(ts)), "plan_us_min": float(min(ts)),
-            "fills": int(st[0]), "moves": int(st[1]), "status": int(st[2])}
+            "fills": int(st[0]), "moves": int(st[1]), "status": int(st[2]),
+            "max_redundant": int(v["n_redundant"].max().item())}
 
 
 def main():
@@ -539,10 +546,22 @@ def main():
         "roofline": roofline,
         "rooflines": roof,
     }
+    log("planner policies at the bench shape")
+    pol = {}
+    for t in W.MAXVIO_SWEEP["bench"]:
+        ids_t2 = W.routing_zipf(shape, t)[0]
+        pol["maxvio_%g" % t] = {
+            "ascending": plan_latency(shape, t, policy=mx.PLAN_ASCENDING, ids=ids_t2),
+            "largest_first": plan_latency(shape, t, policy=mx.PLAN_LARGEST_FIRST, ids=ids_t2)}
+    line["plan_policies"] = pol
     log("plan latency at the Large-E shape")
-    line["plan_large_e"] = {"workload": "Large-E: R=64, S=4096, E=896, K=16, B=14 (plan only)",
-                            "maxvio_1": plan_latency(W.LARGE_E, 1.0),
-                            "maxvio_10": plan_latency(W.LARGE_E, 10.0)}
+    le = {"workload": "Large-E: R=64, S=4096, E=896, K=16, B=14 (plan only)"}
+    for t in W.MAXVIO_SWEEP["large_e"]:
+        ids_le = W.routing_zipf(W.LARGE_E, t)[0]
+        le["maxvio_%g" % t] = {
+            "ascending": plan_latency(W.LARGE_E, t, policy=mx.PLAN_ASCENDING, ids=ids_le),
+            "largest_first": plan_latency(W.LARGE_E, t, policy=mx.PLAN_LARGEST_FIRST, ids=ids_le)}
+    line["plan_large_e"] = le
     log("data backward")
     bms = measure_backward(path, max(3, args.steps // 2), 1)
     bwd = []

@@ -5,6 +5,7 @@
  * in one GPU's memory):
  *
  *   moe_plan_run         router histogram + Theorem-1 planner + route map
+ *   moe_plan_run_policy  the same with a choice of the donor's experts
  *   moe_prefetch_weight  copy redundant experts into prefetch rows [E, E+B)
  *   moe_dispatch         fused permute into expert-grouped [S*K, H] buffers
  *   moe_grouped_gemm     grouped GEMM over the [E+B, H, H'] weight view
@@ -143,6 +144,27 @@ int moe_plan_sizes(const moe_cfg *cfg, size_t sizes_out[MOE_PLAN_NARRAYS]);
  */
 int moe_plan_run(const moe_cfg *cfg, const int32_t *topk_ids,
                  const moe_plan *plan, hipStream_t stream);
+
+/* Donor policies of moe_plan_run_policy. */
+enum {
+  MOE_PLAN_ASCENDING = 0,     /* as moe_plan_run                              */
+  MOE_PLAN_LARGEST_FIRST = 1  /* the donor's largest remaining experts first  */
+};
+
+/*
+ * moe_plan_run with a choice of which home experts a donor gives ("MoonEP :
+ * l'équilibrage parfait", La planification en ligne: the online planner is a
+ * near-optimal heuristic, checked against an offline integer program; Le
+ * théorème: any single donor keeps the E/R bound).  MOE_PLAN_ASCENDING is
+ * moe_plan_run.  MOE_PLAN_LARGEST_FIRST: within a fill, the donor gives the
+ * expert with the most slots still at home in full (ties: lowest id), then
+ * the next, and the last one chosen gives only the part still needed; each
+ * expert still gives its earliest remaining slots, and a fill's moves are
+ * listed in ascending expert id.  Receiver and donor choice, layout and
+ * outputs are as for moe_plan_run.  Any other policy: MOE_EINVAL.
+ */
+int moe_plan_run_policy(const moe_cfg *cfg, const int32_t *topk_ids,
+                        const moe_plan *plan, int32_t policy, hipStream_t stream);
 
 /*
  * prefetch_weight ("Moonshot AI 开源 MoonEP", 核心思想: rows [E, E+B) are local

@@ -16,9 +16,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoonep_h
 MOE_OK, MOE_EINVAL, MOE_EHIP, MOE_ELIMIT = 0, -1, -2, -3
 MODE_TRAIN, MODE_INFER = 0, 1
 STATUS_BAD_ID, STATUS_UNBALANCED, STATUS_CAPACITY, STATUS_INTERNAL = 1, 2, 4, 8
+PLAN_ASCENDING, PLAN_LARGEST_FIRST = 0, 1
 PLAN_FIELDS = ("counts", "load0", "route", "cu_seqlens", "slot_expert",
                "n_redundant", "src_rank", "moves", "status", "workspace")
-ENTRY_POINTS = ("moe_plan_sizes", "moe_plan_run", "moe_prefetch_weight",
+ENTRY_POINTS = ("moe_plan_sizes", "moe_plan_run", "moe_plan_run_policy", "moe_prefetch_weight",
                 "moe_dispatch", "moe_gemm_workspace_size", "moe_grouped_gemm",
                 "moe_combine", "moe_grouped_gemm_wgrad", "moe_reduce_grad",
                 "moe_combine_backward", "moe_grouped_gemm_dgrad",
@@ -62,6 +63,7 @@ def load(path=None):
     sig = {
         "moe_plan_sizes": [C, ctypes.POINTER(SZ)],
         "moe_plan_run": [C, P, PL, P],
+        "moe_plan_run_policy": [C, P, PL, I32, P],
         "moe_prefetch_weight": [C, PL, P, P, P],
         "moe_dispatch": [C, PL, P, P, P],
         "moe_gemm_workspace_size": [C, ctypes.POINTER(SZ)],
@@ -179,6 +181,13 @@ def moe_plan_run(cfg, topk_ids, plan, stream=None):
     n = cfg.R * cfg.S * cfg.K
     ids = _ptr(topk_ids, torch.int32, n, "topk_ids") if n else None
     _check(load().moe_plan_run(ctypes.byref(cfg), ids, plan.c, _stream(stream)), "moe_plan_run")
+
+
+def moe_plan_run_policy(cfg, topk_ids, plan, policy, stream=None):
+    n = cfg.R * cfg.S * cfg.K
+    ids = _ptr(topk_ids, torch.int32, n, "topk_ids") if n else None
+    _check(load().moe_plan_run_policy(ctypes.byref(cfg), ids, plan.c, int(policy),
+                                      _stream(stream)), "moe_plan_run_policy")
 
 
 def moe_prefetch_weight(cfg, plan, w_home, w_pref, stream=None):

@@ -27,7 +27,7 @@ struct IntTag {
 
 struct PlanArgs {
   const int32_t* ids;
-  int32_t N, R, S, E, K, B, mode, n, SK, L, C, M, nbits;
+  int32_t N, R, S, E, K, B, mode, n, SK, L, C, M, nbits, policy;
   int32_t *counts, *load0, *route, *cu, *slot_expert, *n_red, *src_rank, *moves, *status;
   int32_t *cc, *badc, *taken, *home_base, *mptr, *mcnt, *cs_lo, *cs_hi, *cs_base, *cs_dst, *cs_b,
       *cons, *hpre, *spre, *rinfo, *ocum, *misc;
@@ -284,8 +284,65 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       int e0 = co;
       const int eend = (o + 1) * n;
       int ntk = 0, nmc = 0;                     // the new cursor's state
-      // donor gives its home experts in ascending id, earliest slots first
-      while (d > 0) {
+      if (a.policy == MOE_PLAN_LARGEST_FIRST) {
+        // Largest remaining first: the expert of the donor with the most
+        // slots still at home (ties: lowest id), then the next, until the
+        // need is met; only the last one chosen (L) gives part of its slots.
+        // Pass 1 finds L and that part by selecting in descending order of
+        // (remaining, -id); pass 2 walks the donor's experts in ascending
+        // id and moves every expert ranked above L in full, and L's part.
+        typedef __attribute__((address_space(3))) volatile int lds_vint;
+        lds_vint* vT = (lds_vint*)sT;
+        lds_vint* vTaken = (lds_vint*)sTaken;
+        lds_vint* vMcnt = (lds_vint*)sMcnt;
+        const int eb = o * n;
+        // with at most 64 home experts the donor's remaining counts are read
+        // once into registers (pass 1 does not change them)
+        const int x0 = (n <= kWave && lane < n) ? vT[eb + lane] - vTaken[eb + lane] : 0;
+        int prev_r = 0x7fffffff, prev_e = -1, L = -1, Lr = 0, Lamt = 0;
+        for (int it = 0; it < n && d > 0; ++it) {
+          int best_r = 0, best_e = 0x7fffffff;
+          for (int c0 = eb; c0 < eend; c0 += kWave) {
+            const int e = c0 + lane;
+            int r = -1;
+            if (e < eend) {
+              const int x = n <= kWave ? x0 : vT[e] - vTaken[e];
+              if (x > 0 && (x < prev_r || (x == prev_r && e > prev_e))) r = x;
+            }
+            const int mx = wave_max(r);
+            if (mx <= 0) continue;                                  // uniform
+            const uint64_t bal = __ballot(r == mx);
+            const int ce = c0 + __ffsll((unsigned long long)bal) - 1;
+            if (mx > best_r || (mx == best_r && ce < best_e)) { best_r = mx; best_e = ce; }
+          }
+          if (best_r <= 0) break;
+          if (best_r >= d) { L = best_e; Lr = best_r; Lamt = d; d = 0; }
+          else { d -= best_r; prev_r = best_r; prev_e = best_e; }
+        }
+        if (d > 0 || L < 0) { err |= MOE_STATUS_INTERNAL; break; }
+        for (int c0 = eb; c0 < eend; c0 += kWave) {
+          const int e = c0 + lane;
+          int tk = 0, w = 0, take = 0;
+          if (e < eend) {
+            tk = vTaken[e];
+            w = vMcnt[e];
+            const int x = vT[e] - tk;
+            if (e == L) take = Lamt;
+            else if (x > 0 && (x > Lr || (x == Lr && e < L))) take = x;
+          }
+          const uint64_t mvb = __ballot(take > 0);
+          if (take > 0) {
+            const int idx = nm + (int)__popcll(mvb & lt);
+            if (idx < M) { sMe[idx] = e; sMu[idx] = u; sMlo[idx] = tk; sMhi[idx] = tk + take; sMpos[idx] = w; }
+            vTaken[e] = tk + take;
+            vMcnt[e] = w + 1;
+          }
+          nm += (int)__popcll(mvb);
+        }
+      }
+      // ascending: the donor gives its home experts in ascending id,
+      // earliest slots first
+      while (a.policy != MOE_PLAN_LARGEST_FIRST && d > 0) {
         if (e0 >= eend) { err |= MOE_STATUS_INTERNAL; break; }
         const int e = e0 + lane;
         const bool in = e < eend;
@@ -711,10 +768,11 @@ extern "C" int moe_plan_sizes(const moe_cfg* cfg, size_t sizes_out[MOE_PLAN_NARR
   return MOE_OK;
 }
 
-extern "C" int moe_plan_run(const moe_cfg* cfg, const int32_t* topk_ids, const moe_plan* plan,
-                            hipStream_t stream) {
+extern "C" int moe_plan_run_policy(const moe_cfg* cfg, const int32_t* topk_ids,
+                                   const moe_plan* plan, int32_t policy, hipStream_t stream) {
   int rc = check_cfg(cfg);
   if (rc != MOE_OK) return rc;
+  if (policy != MOE_PLAN_ASCENDING && policy != MOE_PLAN_LARGEST_FIRST) return MOE_EINVAL;
   if (!plan_ptrs_ok(plan)) return MOE_EINVAL;
   const PlanLayout L = plan_layout(cfg);
   if (L.N > 0 && (!topk_ids || !plan->route)) return MOE_EINVAL;
@@ -725,6 +783,7 @@ extern "C" int moe_plan_run(const moe_cfg* cfg, const int32_t* topk_ids, const m
   a.n = cfg->E / cfg->R;
   a.SK = cfg->S * cfg->K;
   a.L = L.L; a.C = L.C; a.M = L.M; a.nbits = L.nbits;
+  a.policy = policy;
   a.counts = plan->counts; a.load0 = plan->load0; a.route = plan->route; a.cu = plan->cu_seqlens;
   a.slot_expert = plan->slot_expert; a.n_red = plan->n_redundant; a.src_rank = plan->src_rank;
   a.moves = plan->moves; a.status = plan->status;
@@ -764,6 +823,11 @@ extern "C" int moe_plan_run(const moe_cfg* cfg, const int32_t* topk_ids, const m
       hipLaunchKernelGGL((k_route<false>), dim3(L.C), dim3(kPlanThreads), lds_route, stream, a);
   }
   return hip_status();
+}
+
+extern "C" int moe_plan_run(const moe_cfg* cfg, const int32_t* topk_ids, const moe_plan* plan,
+                            hipStream_t stream) {
+  return moe_plan_run_policy(cfg, topk_ids, plan, MOE_PLAN_ASCENDING, stream);
 }
 
 extern "C" const char* moe_strerror(int code) {

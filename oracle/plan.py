@@ -108,7 +108,10 @@ def stable_rank(topk_ids, E):
     return p
 
 
-def theorem1_fills(counts, cfg):
+POLICY_ASCENDING, POLICY_LARGEST = 0, 1
+
+
+def theorem1_fills(counts, cfg, policy=POLICY_ASCENDING):
     """The constructive procedure of Theorem 1, made deterministic.
 
     [K3-blog] "定理 1" / [MoonEP-fr] "Le théorème": while some rank holds
@@ -117,6 +120,18 @@ def theorem1_fills(counts, cfg):
     overloaded, become balanced, or become underloaded and go back to the
     pool.  Each fill balances one rank for good, so there are at most R-1
     fills, and each receiver's remote slots come from a single rank.
+
+    Which of the donor's home experts give the slots:
+      POLICY_ASCENDING -- ascending id, continuing from where the donor's
+        previous donation stopped (the construction as the proof states it);
+      POLICY_LARGEST -- the expert with the most slots still at home first
+        (ties: lowest id), then the next, until the need is met.  Theorem 1
+        allows any subset of the donor's experts (the lemma only needs a
+        single donor); the pages' planner is a near-optimal heuristic checked
+        against an offline integer program ([MoonEP-fr] "La planification en
+        ligne"), and taking big experts first needs fewer distinct experts.
+    Either way an expert gives its earliest slots still at home, and a
+    fill's moves are listed in ascending expert id.
 
     Returns (moves, fills, taken) where a move (e, u, lo, hi) gives u the
     slots of expert e with in-expert rank p in [lo, hi).
@@ -138,6 +153,20 @@ def theorem1_fills(counts, cfg):
         need = SK - load[u]
         d = need
         first = len(moves)
+        if policy == POLICY_LARGEST:
+            rem = {e: T[e] - taken[e] for e in range(o * n, (o + 1) * n)}
+            take = {}
+            while d > 0:
+                e = max(rem, key=lambda x: (rem[x], -x))
+                if rem[e] == 0:
+                    raise AssertionError("donor ran out of home slots")
+                m = min(d, rem[e])
+                take[e] = m
+                rem[e] -= m
+                d -= m
+            for e in sorted(take):
+                moves.append((e, u, taken[e], taken[e] + take[e]))
+                taken[e] += take[e]
         while d > 0:
             e = cursor[o]
             # a donor never received slots, so its load is its remaining home
@@ -161,7 +190,7 @@ def theorem1_fills(counts, cfg):
     return mv, fills, np.array(taken, dtype=np.int64)
 
 
-def make_plan(topk_ids, cfg):
+def make_plan(topk_ids, cfg, policy=POLICY_ASCENDING):
     """Full plan: histogram, fills, slot map, cu_seqlens and route.
 
     [K3-blog] "在线规划、零拷贝、静态 shape": the planner fixes every token's
@@ -180,7 +209,7 @@ def make_plan(topk_ids, cfg):
     T = histogram(ids, E)
     load0 = home_loads(T, R)
     p = stable_rank(ids, E)
-    moves, fills, taken = theorem1_fills(T, cfg)
+    moves, fills, taken = theorem1_fills(T, cfg, policy)
 
     n_red = np.zeros(R, np.int64)
     src = np.full(R, -1, np.int64)

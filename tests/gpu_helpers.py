@@ -27,12 +27,15 @@ def cfgs(shape):
     return c, o
 
 
-def gpu_plan(shape, ids_np, plan=None):
+def gpu_plan(shape, ids_np, plan=None, policy=0):
     c, _ = cfgs(shape)
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
     if plan is None:
         plan = mx.Plan(c)
-    mx.moe_plan_run(c, ids, plan)
+    if policy:
+        mx.moe_plan_run_policy(c, ids, plan, policy)
+    else:
+        mx.moe_plan_run(c, ids, plan)
     torch.cuda.synchronize()
     return plan, {k: v.cpu().numpy() for k, v in plan.views().items()}
 

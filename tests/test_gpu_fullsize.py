@@ -2,7 +2,8 @@
 bench times (one grouped-GEMM launch over all ranks), checked on sampled
 outputs the oracle computes one by one:
 
-* bench shape (R=8, S=8192, E=384, K=8, H=7168, H'=2048), maxvio 1: plan
+* bench shape (R=8, S=8192, E=384, K=8, H=7168, H'=2048), maxvio 1, with
+  both planner policies (the bench runs the largest-first one): plan
   bit-exact; dispatch and prefetch bit-exact on sampled rows/slots; grouped
   GEMM on 4096 sampled rows; combine on sampled tokens;
 * Theorem-2 worst case in inference mode (B=4, overflow rows read from home
@@ -61,13 +62,14 @@ def check_prefetch(shape, ref, w_home, w_pref):
                                    w_home[e].view(torch.int16)), (r, b, e)
 
 
-def test_bench_shape_forward():
+@pytest.mark.parametrize("policy", [mx.PLAN_ASCENDING, mx.PLAN_LARGEST_FIRST])
+def test_bench_shape_forward(policy):
     shape = W.BENCH
     c, oc = cfgs(shape)
     ids, gates, _, mv = W.routing_zipf(shape, 1.0)
-    announce("bench forward maxvio", mv)
-    ref = make_plan(ids, oc)
-    plan, g = gpu_plan(shape, ids)
+    announce("bench forward maxvio", mv, "policy", policy)
+    ref = make_plan(ids, oc, policy)
+    plan, g = gpu_plan(shape, ids, policy=policy)
     assert_plan_equal(g, ref, shape)
     x, w_home, w_pref, xperm, y = forward_buffers(shape, 31)
     out = torch.empty((shape.tokens, shape.Hp), dtype=torch.bfloat16, device="cuda")

@@ -118,3 +118,60 @@ def test_bad_ids_set_status_and_route():
     good = ids.reshape(-1)
     good = good[(good >= 0) & (good < shape.E)]
     assert np.array_equal(g["counts"], np.bincount(good, minlength=shape.E))
+
+
+# ---------------------------------------------------------------------------
+# The largest-remaining-first donor policy: bit-exact with the oracle's
+# implementation of the same policy on the same shapes.
+# ---------------------------------------------------------------------------
+def check_policy(shape, ids, policy, plan=None):
+    announce("plan policy", policy, shape.name, shape)
+    c, oc = cfgs(shape)
+    ref = make_plan(ids, oc, policy)
+    if plan is None:
+        plan = mx.Plan(c)
+    mx.moe_plan_run_policy(c, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda(), plan,
+                           policy)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in plan.views().items()}
+    assert_plan_equal(g, ref, shape)
+    return plan, ref
+
+
+def test_largest_policy_tiny_and_edges():
+    plan = None
+    for seed in range(100):
+        ids, _ = W.routing_uniform(W.TINY, salt=seed)
+        plan, _ = check_policy(W.TINY, ids, mx.PLAN_LARGEST_FIRST, plan)
+    for kw in (dict(R=1, B=8), dict(B=1, mode=1), dict(B=0, mode=1), dict(R=64, E=128, S=5, K=3, B=2),
+               dict(E=512, R=4, S=40, K=16, B=128), dict(E=2048, R=8, S=20, K=64, B=256),
+               dict(R=1024, E=1024, S=2, K=2, B=1), dict(R=5, E=1000, S=77, K=9, B=200)):
+        shape = W.TINY.with_(**kw)
+        for seed in range(4):
+            if seed == 3:
+                ids = W.routing_hot(shape)
+            elif seed == 2 and shape.R > 1:
+                ids = W.routing_theorem2(shape)
+            else:
+                ids, _ = W.routing_uniform(shape, salt=seed)
+            check_policy(shape, ids, mx.PLAN_LARGEST_FIRST)
+
+
+@pytest.mark.parametrize("name", ["skewed", "bench", "large_e"])
+def test_largest_policy_sweeps(name):
+    shape = W.SHAPES[name]
+    for t in W.MAXVIO_SWEEP[name]:
+        ids, _, _, _ = W.routing_zipf(shape, t)
+        _, big = check_policy(shape, ids, mx.PLAN_LARGEST_FIRST)
+        asc = make_plan(ids, cfgs(shape)[1])
+        assert big.n_redundant.max() <= asc.n_redundant.max()
+    for adv in (W.ADVERSARIAL, W.ADVERSARIAL_INFER):
+        check_policy(adv, W.routing_theorem2(adv), mx.PLAN_LARGEST_FIRST)
+
+
+def test_policy_rejects_unknown_value():
+    c, _ = cfgs(W.TINY)
+    plan = mx.Plan(c)
+    ids = torch.from_numpy(W.routing_uniform(W.TINY)[0]).cuda()
+    with pytest.raises(mx.MoeError):
+        mx.moe_plan_run_policy(c, ids, plan, 7)

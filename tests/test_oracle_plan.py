@@ -20,7 +20,7 @@ import pytest
 
 import workloads as W
 from oracle import metrics, optimum
-from oracle.plan import Cfg, make_plan, stable_rank, histogram
+from oracle.plan import POLICY_LARGEST, Cfg, make_plan, stable_rank, histogram
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
 
@@ -75,12 +75,14 @@ def check_invariants(ids, cfg, plan):
         assert B >= plan.n_redundant.max(initial=0)
 
 
-def queue_simulation(ids, cfg):
+def queue_simulation(ids, cfg, largest=False):
     """Slot-by-slot replay of the fill rules (independent formulation).
 
     Each rank keeps a queue of the slots of its home experts ordered by
     (expert, slot index).  A fill pops d slots from the front of the donor's
-    queue.  Rank buffers are then ordered by (weight row, slot index).
+    queue -- or, with ``largest``, repeatedly pops the front slots of the
+    donor's expert with the most slots left (ties: lowest id) until d slots
+    moved.  Rank buffers are then ordered by (weight row, slot index).
     """
     R, E, SK, n, B = cfg.R, cfg.E, cfg.SK, cfg.n, cfg.B
     flat = ids.reshape(-1).tolist()
@@ -94,8 +96,23 @@ def queue_simulation(ids, cfg):
         u = min(r for r in range(R) if load[r] < SK)
         o = max(range(R), key=lambda r: (load[r], -r))
         d = SK - load[u]
-        for _ in range(d):
-            holder[queues[o].popleft()] = u
+        if largest:
+            left = collections.Counter(flat[i] for i in queues[o])
+            moved = set()
+            todo = d
+            while todo:
+                e = min(left, key=lambda x: (-left[x], x))
+                k = min(todo, left[e])
+                todo -= k
+                left[e] -= k
+                taken_e = [i for i in queues[o] if flat[i] == e][:k]
+                moved.update(taken_e)
+                for i in taken_e:
+                    holder[i] = u
+            queues[o] = collections.deque(i for i in queues[o] if i not in moved)
+        else:
+            for _ in range(d):
+                holder[queues[o].popleft()] = u
         load[o] -= d
         load[u] = SK
         fills += 1
@@ -284,3 +301,49 @@ def test_bench_shape_sweep_invariants():
         assert plan.n_redundant.max() <= shape.n
         assert len(plan.fills) <= shape.R - 1
         assert math.isclose(metrics.maxvio(plan.counts, shape.R, shape.S, shape.K), mv)
+
+
+# ---------------------------------------------------------------------------
+# The largest-remaining-first donor policy (the same theorem, another choice
+# of the donor's experts): same invariants, an independent slot-level replay,
+# and its redundancy against the offline integer program.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R,S,E,K,B,mode", [
+    (4, 16, 8, 2, 2, 0), (3, 7, 9, 3, 3, 0), (5, 11, 10, 4, 1, 1),
+    (6, 5, 12, 5, 0, 1), (2, 9, 8, 8, 4, 0), (8, 4, 16, 3, 2, 0)])
+def test_largest_policy_queue_replay(R, S, E, K, B, mode):
+    shape = W.TINY.with_(R=R, S=S, E=E, K=K, B=B, mode=mode)
+    cfg = cfg_of(shape)
+    for seed in range(40):
+        if seed % 4 == 3:
+            ids = W.routing_hot(shape)
+        else:
+            ids, _ = W.routing_uniform(shape, salt=seed)
+        plan = make_plan(ids, cfg, POLICY_LARGEST)
+        check_invariants(ids, cfg, plan)
+        route, fills = queue_simulation(ids, cfg, largest=True)
+        assert np.array_equal(route, plan.route)
+        assert fills == len(plan.fills)
+
+
+def test_largest_policy_sweeps_and_milp():
+    # same invariants on the skewed and bench sweeps and the Theorem-2 case;
+    # on the skewed sweep the largest-first plan's worst rank needs exactly
+    # what the integer program finds optimal, and never more than ascending
+    for shape, targets in ((W.SKEWED, W.MAXVIO_SWEEP["skewed"]),
+                           (W.BENCH, W.MAXVIO_SWEEP["bench"])):
+        cfg = cfg_of(shape)
+        for t in targets:
+            ids, _, _, _ = W.routing_zipf(shape, t)
+            big = make_plan(ids, cfg, POLICY_LARGEST)
+            asc = make_plan(ids, cfg)
+            check_invariants(ids, cfg, big)
+            assert big.n_redundant.max() <= asc.n_redundant.max()
+            assert len(big.moves) <= len(asc.moves)
+            if shape is W.SKEWED:
+                assert big.n_redundant.max() == optimum.milp_opt(big.counts, shape.R, shape.SK)
+    shape = W.ADVERSARIAL
+    ids = W.routing_theorem2(shape)
+    big = make_plan(ids, cfg_of(shape), POLICY_LARGEST)
+    check_invariants(ids, cfg_of(shape), big)
+    assert big.n_redundant[0] == 42                   # the Theorem-2 worst case is tight
