@@ -130,6 +130,47 @@ def summarize_traffic(fetch_csv, write_csv, cmd_fetch, cmd_write):
     return out
 
 
+def summarize_pmc(sq_csv, tcc_csv, cmd_sq, cmd_tcc, out_md):
+    """Two rocprofv3 --pmc counter CSVs -> clock, matrix-pipe and L2 summary."""
+    import csv
+    def per_kernel(path):
+        acc, dur = {}, {}
+        for r in csv.DictReader(open(path)):
+            k = _short_kernel(r["Kernel_Name"])
+            if not k or k == "copyBuffer":
+                continue
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, {})[r["Dispatch_Id"]] = (float(r["End_Timestamp"]) -
+                                                       float(r["Start_Timestamp"]))
+        mean = lambda v: sum(v) / len(v)
+        return ({k: {c: mean(v) for c, v in cs.items()} for k, cs in acc.items()},
+                {k: mean(list(v.values())) for k, v in dur.items()})
+    sq, dur = per_kernel(sq_csv)
+    tcc, _ = per_kernel(tcc_csv)
+    lines = ["# Clock, matrix pipe and L2 at the bench shape (rocprofv3 --pmc)", "",
+             "Commands (`<repo>` = repository root, `<out>` = output directory):", "",
+             "- `%s`" % cmd_sq, "- `%s`" % cmd_tcc, "",
+             "Summary written by `python bench.py --summarize-pmc`.  Per kernel, averaged over its "
+             "dispatches: clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel time; matrix pipe busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8); waiting = "
+             "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS). "
+             "Kernel times are under the profiler.", "",
+             "| kernel | time us | clock GHz | matrix pipe busy | waves waiting | L2 hit rate |",
+             "|---|---|---|---|---|---|"]
+    for k in sorted(sq):
+        m, t = sq[k], tcc.get(k, {})
+        if "GRBM_GUI_ACTIVE" not in m or k not in dur or dur[k] <= 0:
+            continue
+        active = m["GRBM_GUI_ACTIVE"] / 8
+        hit = t.get("TCC_HIT_sum", 0.0)
+        tot = hit + t.get("TCC_MISS_sum", 0.0)
+        lines.append("| %s | %.0f | %.2f | %.3f | %.3f | %s |" % (
+            k, dur[k] / 1e3, active / dur[k], m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / active,
+            m["SQ_WAIT_INST_ANY"] / max(m["SQ_WAVE_CYCLES"], 1.0),
+            ("%.3f" % (hit / tot)) if tot else "-"))
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def summarize_stats(stats_csv, cmd, out_md):
     """rocprofv3 --kernel-trace --stats kernel_stats.csv -> a short markdown table."""
     import csv
@@ -450,6 +491,9 @@ def main():
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "CMD", "OUT_MD"),
                     help="write a kernel-time summary from rocprofv3 --stats and exit")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("SQ_CSV", "TCC_CSV", "CMD_SQ", "CMD_TCC",
+                                                      "OUT_MD"),
+                    help="write the clock / matrix-pipe / L2 summary from two --pmc runs and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size "
                          "reference for hardware byte counters)")
@@ -459,6 +503,9 @@ def main():
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the R expert-parallel ranks are virtual ranks "
