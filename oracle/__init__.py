@@ -32,6 +32,8 @@ Modules:
 * :mod:`oracle.dataflow` -- dispatch, prefetch, grouped GEMM, combine,
   weight-grad GEMM and reduce_grad, and the data backward (combine_backward,
   dgrad, dispatch_backward), in float64.
+* :mod:`oracle.swiglu`   -- the two-projection SwiGLU expert: first
+  projection fused with the activation, and the activation's backward.
 * :mod:`oracle.optimum`  -- minimum achievable max-redundancy on tiny inputs
   (brute force with a Hall-condition feasibility test, and a SciPy MILP), the
   per-rank lower bound and the Theorem-2 bound.
