@@ -13,7 +13,10 @@ point is also bracketed by HIP events on the stream it runs on, giving each
 step's average duration.  After the timed steps the data backward of the
 layer (combine backward -> data-gradient GEMM -> dispatch backward) is timed
 the same way and reported beside the step ("data_backward"), outside
-`value`.  Prints one JSON line.
+`value`, and so are the two-projection SwiGLU expert's kernels at the same
+shape ("swiglu_expert": first projection [E+B, 7168, 2*2048] fused with
+the activation, second projection [E+B, 2048, 7168], activation backward).
+Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
                     [--sweep] [--no-cpu-baseline]
@@ -51,6 +54,8 @@ TRAFFIC_FILE = os.path.join(PROFILES, "traffic_bench_shape.txt")
 KERNEL_SOURCES = {"k_gemm<0>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<1>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<2>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_gemm<3>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_swiglu_bwd": "moe_expert_load_amd/csrc/swiglu.hip",
                   "k_combine_bwd": "moe_expert_load_amd/csrc/copy.hip",
                   "k_dispatch_bwd": "moe_expert_load_amd/csrc/copy.hip",
                   "k_dispatch": "moe_expert_load_amd/csrc/copy.hip",
@@ -438,6 +443,78 @@ def measure_dedup(path, steps):
     }
 
 
+def measure_swiglu(path, steps):
+    """Kernels of the two-projection SwiGLU expert at the bench shape.
+
+    H' = 2048 is the intermediate size: W13 [E+B, 7168, 4096] (gate | up),
+    W2 [E+B, 2048, 7168].  Times the fused first projection with and without
+    the stored h13, the plain grouped GEMM over the same [H, 2H'] weights
+    (same flops, plain epilogue), the second projection and the activation
+    backward, each averaged over ``steps`` launches after one warm-up.
+    """
+    s, p, c = path.shape, path.plan, path.c
+    Hi, dev, rows = s.Hp, "cuda", s.R * s.SK
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    c13 = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, 2 * Hi, s.B, s.mode)
+    c2 = mx.make_cfg(s.R, s.S, s.E, s.K, Hi, s.H, s.B, s.mode)
+    w13 = W.randn_bf16((s.E, s.H, 2 * Hi), 11, dev, chunk_rows=1)
+    w13p = torch.empty((s.R * s.B, s.H, 2 * Hi), **bf)
+    w2 = W.randn_bf16((s.E, Hi, s.H), 12, dev, chunk_rows=1)
+    w2p = torch.empty((s.R * s.B, Hi, s.H), **bf)
+    act, h13, dh13 = (torch.empty((rows, Hi), **bf), torch.empty((rows, 2 * Hi), **bf),
+                      torch.empty((rows, 2 * Hi), **bf))
+    y2 = torch.empty((rows, s.H), **bf)
+    dact = W.randn_bf16((rows, Hi), 13, dev)
+    ws = torch.empty(max(mx.moe_gemm_workspace_size(x) for x in (c13, c2)), dtype=torch.uint8,
+                     device=dev)
+    mx.moe_prefetch_weight(c13, p, w13, w13p)
+    mx.moe_prefetch_weight(c2, p, w2, w2p)
+    flop_up, flop_down = 2.0 * s.H * 2 * Hi * rows, 2.0 * Hi * s.H * rows
+    calls = (
+        ("swiglu_gemm", "k_gemm<3>", "flops", flop_up,
+         lambda: mx.moe_grouped_gemm_swiglu(c, path.xperm, w13, w13p, p.cu_seqlens, act, h13,
+                                            0, s.R, ws)),
+        ("swiglu_gemm_act_only", "k_gemm<3>", "flops", flop_up,
+         lambda: mx.moe_grouped_gemm_swiglu(c, path.xperm, w13, w13p, p.cu_seqlens, act, None,
+                                            0, s.R, ws)),
+        ("plain_gemm_2h", "k_gemm<0>", "flops", flop_up,
+         lambda: mx.moe_grouped_gemm(c13, path.xperm, w13, w13p, p.cu_seqlens, h13, 0, s.R, ws)),
+        ("down_gemm", "k_gemm<0>", "flops", flop_down,
+         lambda: mx.moe_grouped_gemm(c2, act, w2, w2p, p.cu_seqlens, y2, 0, s.R, ws)),
+        # read h13 and d act, write d h13
+        ("swiglu_bwd", "k_swiglu_bwd", "bytes", 10.0 * Hi * rows,
+         lambda: mx.moe_swiglu_backward(c, h13, dact, dh13)),
+    )
+    out = {"workload": "bench shape, SwiGLU expert: W13 [E+B, 7168, 4096] (gate | up), "
+                       "W2 [E+B, 2048, 7168], %d rows" % rows}
+    for name, kern, kind, amount, f in calls:
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.mean(ts))
+        if kind == "flops":
+            ach = amount / (ms * 1e-3) / 1e12
+            out[name] = {"kernel": kern, "bound": "mfma", "ms": ms, "achieved": ach,
+                         "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                         "frac": ach / BF16_PEAK_TFLOPS}
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            out[name] = {"kernel": kern, "bound": "hbm", "ms": ms, "achieved": ach,
+                         "unit": "GB/s", "peak": HBM_PEAK_GBPS, "frac": ach / HBM_PEAK_GBPS}
+    del w13, w13p, w2, w2p, act, h13, dh13, y2, dact, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_backward(path, steps, warmup):
     path.run(warmup, timed=False, backward=True)
     torch.cuda.synchronize()
@@ -629,6 +706,8 @@ def main():
     line["data_backward"] = bwd
     log("dedup dispatch")
     line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
+    log("swiglu expert")
+    line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
     if args.sweep:
         sweep = {}
         for t in W.MAXVIO_SWEEP["bench"]:

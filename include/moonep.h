@@ -24,6 +24,18 @@
  *   moe_route_encode     route map with repeats on a rank as -(row)-1
  *   moe_dispatch_dedup   payload once per (token, rank), then local copies
  *
+ * and the two-projection SwiGLU expert:
+ *
+ *   moe_grouped_gemm_swiglu  first projection [E+B, H, 2H'] fused with
+ *                            act = silu(gate) * up
+ *   moe_swiglu_backward      gradients of the activation
+ *
+ * Every projection of an expert is its own [E+B, H_in, H_out] weight view;
+ * the GEMM, prefetch, wgrad, dgrad, combine and reduce_grad entry points take
+ * the projection's widths as cfg->H (input) and cfg->Hp (output), so a down
+ * projection [E+B, H', H] passes a moe_cfg with H = H' and Hp = H.  The plan
+ * does not depend on H or Hp and serves every projection of the layer.
+ *
  * Sources: "Kimi K3 模型结构（8）：训练并行，MoonEP 与四类等待" (blog.javazero.top),
  * "Moonshot AI 开源 MoonEP" (feinterview), "MoonEP : l'équilibrage parfait"
  * (mkdocs.reaper.mx), "大规模 LLM 训练系统研究账本" (llm-atlas); each entry
@@ -317,6 +329,42 @@ int moe_route_encode(const moe_cfg *cfg, const moe_plan *plan, int32_t *route_en
  */
 int moe_dispatch_dedup(const moe_cfg *cfg, const int32_t *route_enc,
                        const moe_bf16 *x, moe_bf16 *xperm, hipStream_t stream);
+
+/*
+ * First projection of a two-projection SwiGLU expert ("Moonshot AI 开源
+ * MoonEP", 核心思想: each expert projection is one contiguous [E+B, H, H']
+ * tensor addressed by row index; H' is the expert FFN's intermediate size).
+ * cfg->Hp = H'.  W13(r, j) = [W_gate | W_up] is [H][2H'] bf16 (gate columns
+ * [0, H'), up columns [H', 2H')), from w13_home [E][H][2H'] for j < E and
+ * w13_pref [R][B][H][2H'] otherwise (fill it with moe_prefetch_weight and a
+ * cfg whose Hp is 2H').  For ranks r in [rank_begin, rank_end) and every
+ * non-empty segment j, with fp32 accumulation:
+ *   gate = xperm_seg @ W_gate,  up = xperm_seg @ W_up
+ *   act[r][cu[j]:cu[j+1]] = bf16( silu(gate) * up ),  silu(z) = z / (1 + e^-z)
+ *   h13[r][cu[j]:cu[j+1]] = [ bf16(gate) | bf16(up) ]  (only if h13 != NULL)
+ * act [R][S*K][H'], h13 [R][S*K][2H'] (kept for moe_swiglu_backward),
+ * xperm [R][S*K][H].  Rows outside the listed ranks are not written.
+ * `workspace` as for moe_grouped_gemm.  Requires H * H' * 4 < 2^32
+ * (else MOE_ELIMIT).
+ */
+int moe_grouped_gemm_swiglu(const moe_cfg *cfg, const moe_bf16 *xperm,
+                            const moe_bf16 *w13_home, const moe_bf16 *w13_pref,
+                            const int32_t *cu_seqlens, moe_bf16 *act, moe_bf16 *h13,
+                            int32_t rank_begin, int32_t rank_end, void *workspace,
+                            hipStream_t stream);
+
+/*
+ * Gradients of the SwiGLU activation (same source; act = silu(gate) * up).
+ * cfg->Hp = H'.  For all R*S*K rows, from the stored h13 = [gate | up] and
+ * dact, with s = 1 / (1 + e^-gate) computed in fp32:
+ *   dh13[:, :H'] = bf16( dact * up * s * (1 + gate * (1 - s)) )   (d gate)
+ *   dh13[:, H':] = bf16( dact * gate * s )                        (d up)
+ * h13, dh13 [R][S*K][2H'] bf16, dact [R][S*K][H'] bf16.  dh13 may be h13
+ * (in place); it must not overlap dact otherwise.  All three 16-byte aligned
+ * (else MOE_EINVAL).
+ */
+int moe_swiglu_backward(const moe_cfg *cfg, const moe_bf16 *h13, const moe_bf16 *dact,
+                        moe_bf16 *dh13, hipStream_t stream);
 
 /* Host only.  Static text for a MOE_* return code. */
 const char *moe_strerror(int code);

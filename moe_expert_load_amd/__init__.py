@@ -24,7 +24,7 @@ ENTRY_POINTS = ("moe_plan_sizes", "moe_plan_run", "moe_plan_run_policy", "moe_pr
                 "moe_combine", "moe_grouped_gemm_wgrad", "moe_reduce_grad",
                 "moe_combine_backward", "moe_grouped_gemm_dgrad",
                 "moe_dispatch_backward", "moe_route_encode", "moe_dispatch_dedup",
-                "moe_strerror")
+                "moe_grouped_gemm_swiglu", "moe_swiglu_backward", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -76,6 +76,8 @@ def load(path=None):
         "moe_dispatch_backward": [C, PL, P, P, P],
         "moe_route_encode": [C, PL, P, P],
         "moe_dispatch_dedup": [C, P, P, P, P],
+        "moe_grouped_gemm_swiglu": [C, P, P, P, P, P, P, I32, I32, P, P],
+        "moe_swiglu_backward": [C, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -267,6 +269,34 @@ def moe_grouped_gemm_dgrad(cfg, dy, w_home, w_pref, cu_seqlens, dxperm, rank_beg
             _ptr(workspace, torch.uint8, moe_gemm_workspace_size(cfg), "workspace"),
             _stream(stream))
     _check(load().moe_grouped_gemm_dgrad(*args), "moe_grouped_gemm_dgrad")
+
+
+def moe_grouped_gemm_swiglu(cfg, xperm, w13_home, w13_pref, cu_seqlens, act, h13, rank_begin,
+                            rank_end, workspace, stream=None):
+    """cfg.Hp is the intermediate size H'; W13 rows are [H][2H'] (gate | up)."""
+    SK = cfg.S * cfg.K
+    hh = cfg.H * 2 * cfg.Hp
+    args = (ctypes.byref(cfg),
+            _ptr(xperm, torch.bfloat16, cfg.R * SK * cfg.H, "xperm"),
+            _ptr(w13_home, torch.bfloat16, cfg.E * hh, "w13_home"),
+            _ptr(w13_pref, torch.bfloat16, cfg.R * cfg.B * hh, "w13_pref") if cfg.B else None,
+            _ptr(cu_seqlens, torch.int32, cfg.R * (cfg.E + cfg.B + 1), "cu_seqlens"),
+            _ptr(act, torch.bfloat16, cfg.R * SK * cfg.Hp, "act"),
+            _ptr(h13, torch.bfloat16, cfg.R * SK * 2 * cfg.Hp, "h13"),
+            int(rank_begin), int(rank_end),
+            _ptr(workspace, torch.uint8, moe_gemm_workspace_size(cfg), "workspace"),
+            _stream(stream))
+    _check(load().moe_grouped_gemm_swiglu(*args), "moe_grouped_gemm_swiglu")
+
+
+def moe_swiglu_backward(cfg, h13, dact, dh13, stream=None):
+    rows = cfg.R * cfg.S * cfg.K
+    args = (ctypes.byref(cfg),
+            _ptr(h13, torch.bfloat16, rows * 2 * cfg.Hp, "h13"),
+            _ptr(dact, torch.bfloat16, rows * cfg.Hp, "dact"),
+            _ptr(dh13, torch.bfloat16, rows * 2 * cfg.Hp, "dh13"),
+            _stream(stream))
+    _check(load().moe_swiglu_backward(*args), "moe_swiglu_backward")
 
 
 def moe_dispatch_backward(cfg, plan, dxperm, dx, stream=None):

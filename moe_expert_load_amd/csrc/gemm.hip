@@ -21,7 +21,12 @@
 //               tiles in that XCD's L2.
 //   MODE 0: y = xperm_seg @ W (forward); MODE 1: G = xperm_seg^T @ dy_seg
 //   (weight gradient, fp32); MODE 2: dxperm_seg = dy_seg @ W^T (data
-//   gradient, over the forward's work list).
+//   gradient, over the forward's work list); MODE 3: the first projection
+//   of a SwiGLU expert, act = silu(x W_gate) * (x W_up) with W13 = [W_gate |
+//   W_up] in one [E+B, H, 2H'] tensor -- each 256-column tile takes 128
+//   gate and the same 128 up columns, interleaved in 32-column blocks, so
+//   every wave holds gate and up of the same outputs in its accumulators
+//   and applies the activation in registers.
 // Tile: BM = BN = 256, BK = 32; 4 waves in a 2x2 grid, each 128x128 =
 // 4x4 MFMA blocks of 32x32 with fp32 accumulators (256 AGPRs per wave).
 // Operands go from global memory straight into LDS (buffer_load ... lds,
@@ -59,7 +64,7 @@ constexpr int BM = 256, BN = 256;
 #endif
 constexpr int kGemmThreads = 256;
 
-enum { MODE_FWD = 0, MODE_WGRAD = 1, MODE_DGRAD = 2 };
+enum { MODE_FWD = 0, MODE_WGRAD = 1, MODE_DGRAD = 2, MODE_SWIGLU = 3 };
 
 struct WorkItem {
   int32_t r, j, row0, rows;  // rank, weight row, first xperm row (absolute), row count
@@ -71,7 +76,9 @@ struct GemmArgs {
   const uint16_t* w_home;
   const uint16_t* w_pref;
   const uint16_t* dy;
-  uint16_t* y;                // forward output; the data gradient's output (dxperm)
+  uint16_t* y;                // forward output; the data gradient's output (dxperm);
+                              // the SwiGLU forward's activation
+  uint16_t* h13;              // SwiGLU forward: gate and up outputs (optional)
   float* grad_home;
   float* grad_pref;
   const WorkItem* items;
@@ -205,6 +212,16 @@ __device__ __forceinline__ unsigned char* epilogue_area(int wv) {
 #endif
 }
 
+// A second per-wave 16 KB area, disjoint from every epilogue_area (the
+// SwiGLU epilogue stages gate and up there beside the activation).
+__device__ __forceinline__ unsigned char* epilogue_area2(int wv) {
+#if MOONEP_GEMM_STAGES >= 4
+  return wv == 0 ? g_sb0 : wv == 1 ? g_sb1 : wv == 2 ? g_sb2 : g_sb3;
+#else
+  return epilogue_area(wv) + 16384;     // the 2-stage arrays are 32 KB each
+#endif
+}
+
 // Workgroup barrier that orders this wave's LDS accesses around it but does
 // not wait for outstanding global loads (the direct-to-LDS loads of later
 // stages stay in flight; each wave waits for its own with wait_vm first).
@@ -247,11 +264,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   // Paired A tiles pay off where both operands are row tiles (the data
   // gradient: +5 %); the forward measured the same either way.
   constexpr bool kPair = MODE == MODE_DGRAD && MOONEP_GEMM_PAIRA && BK == 32 && kNST == 4;
-  constexpr bool kNMajor = MODE == MODE_DGRAD || (MODE == MODE_FWD && MOONEP_FWD_NMAJOR);
+  constexpr bool kSwi = MODE == MODE_SWIGLU;
+  constexpr bool kNMajor =
+      MODE == MODE_DGRAD || ((MODE == MODE_FWD || kSwi) && MOONEP_FWD_NMAJOR);
   const int H = g.H, Hp = g.Hp;
+  const int WC = kSwi ? 2 * Hp : Hp;                     // weight / dy row length
   const int ntm = MODE == MODE_WGRAD ? (H + BM - 1) / BM : 1;
   const int NOUT = MODE == MODE_DGRAD ? H : Hp;          // output columns
-  const int ntn = (NOUT + BN - 1) / BN;
+  // a SwiGLU tile yields 128 activation columns
+  const int ntn = kSwi ? (Hp + BN / 2 - 1) / (BN / 2) : (NOUT + BN - 1) / BN;
   const int64_t total = int64_t(*g.nitems) * ntm * ntn;
   const int G = gridDim.x, per = G / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       it = item_at(item);
     }
     const int n0 = tn * BN, m0 = tm * BM;
-    const int KD = MODE == MODE_FWD ? H : MODE == MODE_DGRAD ? Hp : it.rows;
+    const int KD = (MODE == MODE_FWD || kSwi) ? H : MODE == MODE_DGRAD ? Hp : it.rows;
     // k-tiles, rounded up to whole passes over the stages: tiles past the
     // end load zeros (range-checked loads; ragged forward K is zeroed below)
     const int nk = ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
@@ -341,9 +362,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     const uint16_t* Bbase;
     uint32_t bbytes;
     if (MODE != MODE_WGRAD) {
-      Bbase = it.j < g.E ? g.w_home + int64_t(it.j) * H * Hp
-                         : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
-      bbytes = uint32_t(H) * Hp * 2;
+      Bbase = it.j < g.E ? g.w_home + int64_t(it.j) * H * WC
+                         : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * WC;
+      bbytes = uint32_t(H) * WC * 2;
     } else {
       Bbase = g.dy + int64_t(it.row0) * Hp;
       bbytes = uint32_t(it.rows) * Hp * 2;
@@ -364,8 +385,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       const int cc = (lane & 31) ^ (4 * (crow & 3));
       if (kRowA) goa[u] = uint32_t(rrow) * arow * 2 + rkc * 16;
       else goa[u] = uint32_t(crow) * H * 2 + uint32_t(m0 + 8 * cc) * 2;
+      // SwiGLU: 32-column block b of the tile is gate (b even) or up (b odd)
+      // of activation columns tn*128 + (b/2)*32 + [0, 32).  Columns past the
+      // activation width only feed accumulators that are never stored.
+      const int col = kSwi ? ((cc >> 2) & 1) * Hp + tn * (BN / 2) + (cc >> 3) * 32 + 8 * (cc & 3)
+                           : n0 + 8 * cc;
       if (kRowB) gob[u] = uint32_t(n0 + rrow) * Hp * 2 + rkc * 16;
-      else gob[u] = uint32_t(crow) * Hp * 2 + uint32_t(n0 + 8 * cc) * 2;
+      else gob[u] = uint32_t(crow) * WC * 2 + uint32_t(col) * 2;
     }
 
     // paired A loads: load t (8 per wave) covers rows 8t .. 8t+7, whole lines
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       unsigned char* As = stage_a<S>();
       unsigned char* Bs = stage_b<S>();
       const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
-      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * Hp * 2;
+      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
 #pragma unroll
       for (int u = 0; u < NI; ++u) {
         load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
@@ -404,7 +430,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       unsigned char* As = stage_a<S>();
       unsigned char* Bs = stage_b<S>();
       const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
-      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * Hp * 2;
+      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
 #pragma unroll
       for (int u2 = 0; u2 < NI / 2; ++u2) {
         const int u = h * (NI / 2) + u2;
@@ -416,7 +442,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     auto issue_b = [&](auto S_, int kt) {
       constexpr int S = decltype(S_)::value;
       unsigned char* Bs = stage_b<S>();
-      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * Hp * 2;
+      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
 #pragma unroll
       for (int u = 0; u < NI; ++u) load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
     };
@@ -676,7 +702,66 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 
     // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
     // rows 8*(v/4) + 4*(l/32) + v%4 of its block for v = 0..15.
-    if (MODE != MODE_WGRAD) {
+    if constexpr (kSwi) {
+      // acc[i][2p] = gate and acc[i][2p+1] = up of activation columns
+      // a0 + 32p + lane % 32.  Per half (64 rows), act = silu(gate) * up is
+      // staged as bf16 in the wave's first area (144-byte rows: the two lane
+      // halves, 4 rows apart, land on different banks) and, with h13 given,
+      // gate and up in its second area (128-byte rows); then every staged
+      // row piece goes out as one 16-byte store: act to act[:, a], gate to
+      // h13[:, a], up to h13[:, H' + a].  sigmoid uses the hardware
+      // reciprocal (1 ulp), far inside the bf16 rounding of the output.
+      unsigned char* Ca = epilogue_area(wv);
+      unsigned char* Cg = epilogue_area2(wv);
+      const int a0 = tn * (BN / 2) + wn * 64;
+      const bool keep = g.h13 != nullptr;
+      const int nout = keep ? 3 * 64 * 8 : 64 * 8;
+      uint16_t* actb = g.y + int64_t(it.row0) * Hp;
+      uint16_t* hb = keep ? g.h13 + int64_t(it.row0) * 2 * Hp : nullptr;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int lo = 4 * (lane >> 5), col2 = (lane & 31) * 2;
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const f32x16 ga = acc[2 * half + i2][2 * p], ua = acc[2 * half + i2][2 * p + 1];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int mm = 32 * i2 + 8 * (v >> 2) + (v & 3) + lo;
+              const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-ga[v]));
+              *reinterpret_cast<uint16_t*>(Ca + mm * 144 + 64 * p + col2) =
+                  (uint16_t)f32_to_bf16(ga[v] * sg * ua[v]);
+              if (keep) {
+                *reinterpret_cast<uint16_t*>(Cg + mm * 128 + 64 * p + col2) =
+                    (uint16_t)f32_to_bf16(ga[v]);
+                *reinterpret_cast<uint16_t*>(Cg + 8192 + mm * 128 + 64 * p + col2) =
+                    (uint16_t)f32_to_bf16(ua[v]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 4
+        for (int c = lane; c < nout; c += kWave) {
+          const int which = c >> 9, rr = (c >> 3) & 63, cc = c & 7;
+          const int m = wm * 128 + half * 64 + rr;
+          const int n = a0 + cc * 8;
+          const unsigned char* src = which == 0 ? Ca + rr * 144 + cc * 16
+                                                : Cg + (which - 1) * 8192 + rr * 128 + cc * 16;
+          uint16_t* dst = which == 0 ? actb + uint32_t(m) * Hp + n
+                                     : hb + uint32_t(m) * 2 * Hp + (which - 1) * Hp + n;
+          if (m < it.rows && n < Hp)
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      __syncthreads();
+    } else if (MODE != MODE_WGRAD) {
       // Per wave, two passes of 64 rows x 128 columns staged as bf16 in the
       // wave's own 16 KB stage array (256-byte rows), then whole 16-byte row
       // chunks to global memory (rows of NOUT columns).
@@ -863,6 +948,8 @@ static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hi
   G = std::max(8, G - G % 8);
   if (mode == MODE_FWD)
     hipLaunchKernelGGL((k_gemm<MODE_FWD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+  else if (mode == MODE_SWIGLU)
+    hipLaunchKernelGGL((k_gemm<MODE_SWIGLU>), dim3(G), dim3(kGemmThreads), 0, stream, g);
   else if (mode == MODE_DGRAD)
     hipLaunchKernelGGL((k_gemm<MODE_DGRAD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
   else
@@ -905,6 +992,34 @@ extern "C" int moe_grouped_gemm(const moe_cfg* cfg, const moe_bf16* xperm, const
   g.items = s.items;
   g.nitems = s.nitems;
   return launch_gemm(MODE_FWD, cfg, g, s, stream);
+}
+
+extern "C" int moe_grouped_gemm_swiglu(const moe_cfg* cfg, const moe_bf16* xperm,
+                                       const moe_bf16* w13_home, const moe_bf16* w13_pref,
+                                       const int32_t* cu_seqlens, moe_bf16* act, moe_bf16* h13,
+                                       int32_t rank_begin, int32_t rank_end, void* workspace,
+                                       hipStream_t stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (rank_begin < 0 || rank_end > cfg->R || rank_begin > rank_end) return MOE_EINVAL;
+  // one [H][2H'] weight must fit the 32-bit buffer offsets
+  if (int64_t(cfg->H) * cfg->Hp * 4 >= (int64_t(1) << 32)) return MOE_ELIMIT;
+  if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
+  if (!xperm || !w13_home || !cu_seqlens || !act || !workspace) return MOE_EINVAL;
+  if (cfg->B > 0 && !w13_pref) return MOE_EINVAL;
+  GemmArgs g{};
+  g.xperm = xperm; g.w_home = w13_home; g.w_pref = w13_pref; g.y = act; g.h13 = h13;
+  g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
+  SchedArgs s{};
+  s.cu = cu_seqlens;
+  s.nitems = reinterpret_cast<int32_t*>(workspace);
+  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
+  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
+  s.SK = cfg->S * cfg->K;
+  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
+  g.items = s.items;
+  g.nitems = s.nitems;
+  return launch_gemm(MODE_SWIGLU, cfg, g, s, stream);
 }
 
 extern "C" int moe_grouped_gemm_dgrad(const moe_cfg* cfg, const moe_bf16* dy, const moe_bf16* w_home,

@@ -1,7 +1,8 @@
 """The C-ABI library loads and exports every symbol include/*.h declares.
 
 CPU only: no call here touches a GPU (only the host-only size and error-text
-entry points are called).
+entry points are called, and entry points with arguments their host checks
+reject before anything is launched).
 """
 import ctypes
 import glob
@@ -79,6 +80,26 @@ def test_host_only_calls_and_validation():
     # inference may use fewer slots, even none
     mx.moe_plan_sizes(mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 4, mx.MODE_INFER))
     mx.moe_plan_sizes(mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 0, mx.MODE_INFER))
+    # SwiGLU entry points: host checks come before any launch
+    lib = mx.load()
+    big = mx.make_cfg(8, 16, 8, 2, 65536, 16384, 1)        # H * H' * 4 = 2^32
+    assert lib.moe_grouped_gemm_swiglu(ctypes.byref(big), None, None, None, None, None, None,
+                                       0, 8, None, None) == mx.MOE_ELIMIT
+    small = mx.make_cfg(4, 16, 8, 2, 128, 64, 2)
+    assert lib.moe_grouped_gemm_swiglu(ctypes.byref(small), None, None, None, None, None, None,
+                                       0, 4, None, None) == mx.MOE_EINVAL
+    assert lib.moe_grouped_gemm_swiglu(ctypes.byref(small), None, None, None, None, None, None,
+                                       2, 2, None, None) == mx.MOE_OK      # empty rank range
+    assert lib.moe_grouped_gemm_swiglu(ctypes.byref(small), None, None, None, None, None, None,
+                                       0, 5, None, None) == mx.MOE_EINVAL
+    assert lib.moe_swiglu_backward(ctypes.byref(small), None, None, None, None) == mx.MOE_EINVAL
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 64)
+    # d act overlapping dh13, and a misaligned pointer, are rejected
+    assert lib.moe_swiglu_backward(ctypes.byref(small), ctypes.c_void_p(1 << 30), a, b,
+                                   None) == mx.MOE_EINVAL
+    assert lib.moe_swiglu_backward(ctypes.byref(small), ctypes.c_void_p((1 << 30) + 8),
+                                   ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28),
+                                   None) == mx.MOE_EINVAL
     assert mx.moe_strerror(mx.MOE_EINVAL).startswith("invalid")
     assert mx.moe_strerror(12345) == "unknown error code"
 
