@@ -42,24 +42,25 @@ __global__ __launch_bounds__(256) void k_prefetch(const u32x4* __restrict__ w_ho
 }
 
 // ---------------------------------------------------------------------------
-// dispatch: one wave per token; the row is read once (DU vectors per lane per
-// pass) and written to each of its K destinations.  Plain stores: on gfx950
-// they sustain a higher write rate than non-temporal ones for this pattern.
+// dispatch: one workgroup per token; its 4 waves split the row (Q vectors per
+// lane per pass), read it once and write it to each of its K destinations,
+// so at any moment the workgroup's stores cover one whole destination row.
+// Measured at the bench shape: 4 % faster than one wave per token; plain
+// stores sustain a higher write rate than non-temporal ones here.
 // ---------------------------------------------------------------------------
-template <int DU>
+template <int Q>
 __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
                                                   u32x4* __restrict__ xperm,
-                                                  const int32_t* __restrict__ route, int ntok,
-                                                  int K, int hv) {
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= ntok) return;
-  const int lane = lane_id();
+                                                  const int32_t* __restrict__ route, int K,
+                                                  int hv) {
+  const int t = blockIdx.x;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
   const int myroute = lane < K ? route[int64_t(t) * K + lane] : -1;
   const u32x4* src = x + int64_t(t) * hv;
-  for (int c0 = 0; c0 < hv; c0 += kWave * DU) {
-    u32x4 v[DU];
+  for (int c0 = w * kWave * Q; c0 < hv; c0 += 4 * kWave * Q) {
+    u32x4 v[Q];
 #pragma unroll
-    for (int u = 0; u < DU; ++u) {
+    for (int u = 0; u < Q; ++u) {
       const int c = c0 + u * kWave + lane;
       if (c < hv) v[u] = src[c];
     }
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
       if (dst < 0) continue;
       u32x4* d = xperm + int64_t(dst) * hv;
 #pragma unroll
-      for (int u = 0; u < DU; ++u) {
+      for (int u = 0; u < Q; ++u) {
         const int c = c0 + u * kWave + lane;
         if (c < hv) d[c] = v[u];
       }
@@ -402,19 +403,15 @@ extern "C" int moe_dispatch(const moe_cfg* cfg, const moe_plan* plan, const moe_
   if (ntok == 0) return MOE_OK;
   if (!plan || !plan->route || !x || !xperm) return MOE_EINVAL;
   const int hv = cfg->H / 8;
-  const int du = (hv + kWave - 1) / kWave;
-  const dim3 grid((ntok + 3) / 4), block(256);
+  const int q = (hv + 4 * kWave - 1) / (4 * kWave);   // vectors per lane for one pass
+  const dim3 grid(ntok), block(256);
   const u32x4* xs = reinterpret_cast<const u32x4*>(x);
   u32x4* xd = reinterpret_cast<u32x4*>(xperm);
-#define MOE_DISPATCH(N)                                                                      \
-  hipLaunchKernelGGL(k_dispatch<N>, grid, block, 0, stream, xs, xd, plan->route, ntok, cfg->K, \
-                     hv)
-  if (du <= 1) MOE_DISPATCH(1);
-  else if (du <= 2) MOE_DISPATCH(2);
-  else if (du <= 4) MOE_DISPATCH(4);
-  else if (du <= 8) MOE_DISPATCH(8);
-  else if (du <= 14) MOE_DISPATCH(14);
-  else MOE_DISPATCH(16);
+#define MOE_DISPATCH(N) \
+  hipLaunchKernelGGL(k_dispatch<N>, grid, block, 0, stream, xs, xd, plan->route, cfg->K, hv)
+  if (q <= 1) MOE_DISPATCH(1);
+  else if (q <= 2) MOE_DISPATCH(2);
+  else MOE_DISPATCH(4);                                // larger rows take several passes
 #undef MOE_DISPATCH
   return hip_status();
 }
