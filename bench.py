@@ -15,7 +15,8 @@ layer (combine backward -> data-gradient GEMM -> dispatch backward) is timed
 the same way and reported beside the step ("data_backward"), outside
 `value`, and so are the two-projection SwiGLU expert's kernels at the same
 shape ("swiglu_expert": first projection [E+B, 7168, 2*2048] fused with
-the activation, second projection [E+B, 2048, 7168], activation backward).
+the activation, second projection [E+B, 2048, 7168], activation backward),
+and a two-layer backward sharing one prefetch pool ("prefetch_pool").
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
@@ -515,6 +516,114 @@ def measure_swiglu(path, steps):
     return out
 
 
+def measure_pool(path, reps):
+    """Two layers of one projection sharing one prefetch pool, backward pass.
+
+    The pages' prefetch slots come from one pool shared by all layers: here
+    w_pref and grad_pref of the step serve two layers.  Layer 0 (fresh
+    weights and activations, Theorem-2 routing: the most slots) and layer 1
+    (the step's own buffers and plan) run forward in order, so the pool ends
+    with layer 1's slots.  Their backward runs layer 1 then layer 0; before
+    layer 0's data-gradient GEMM its slots must be prefetched again.  Timed
+    two ways: the re-prefetch serialized on the compute stream, and on a
+    second stream that starts once layer 1's data-gradient GEMM (the last
+    reader of the slots) is done, meant to overlap layer 1's weight gradient,
+    reduce_grad and dispatch backward.  (It cannot: the persistent GEMM
+    keeps one 512-register wave on every SIMD, so no other kernel's waves fit
+    on any CU until it ends; "hidden_ms" measures what overlap there is.)
+    """
+    s, c, dev = path.shape, path.c, "cuda"
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    rows = s.R * s.SK
+    L0 = {"ids": torch.from_numpy(np.ascontiguousarray(W.routing_theorem2(s), np.int32)).to(dev),
+          "gates": torch.from_numpy(W.gates_uniform(s)).to(dev), "plan": mx.Plan(c, dev),
+          "x": W.randn_bf16((s.tokens, s.H), 21, dev),
+          "w": W.randn_bf16((s.E, s.H, s.Hp), 22, dev, chunk_rows=1),
+          "dout": W.randn_bf16((s.tokens, s.Hp), 23, dev),
+          "xperm": torch.empty((rows, s.H), **bf), "y": torch.empty((rows, s.Hp), **bf),
+          "out": torch.empty((s.tokens, s.Hp), **bf),
+          "gh": torch.zeros((s.E, s.H, s.Hp), dtype=torch.float32, device=dev)}
+    L1 = {"ids": path.ids, "gates": path.gates, "plan": path.plan, "x": path.x,
+          "w": path.w_home, "dout": path.dout, "xperm": path.xperm, "y": path.y, "out": path.out,
+          "gh": path.gh}
+    w_pool, g_pool, ws = path.w_pref, path.gp, path.ws
+    compute, copy = torch.cuda.current_stream(), torch.cuda.Stream()   # default priority
+    mx.moe_plan_run_policy(c, L0["ids"], L0["plan"], PLAN_POLICY)
+    for L in (L0, L1):
+        mx.moe_prefetch_weight(c, L["plan"], L["w"], w_pool)
+        mx.moe_dispatch(c, L["plan"], L["x"], L["xperm"])
+        mx.moe_grouped_gemm(c, L["xperm"], L["w"], w_pool, L["plan"].cu_seqlens, L["y"], 0, s.R,
+                            ws)
+        mx.moe_combine(c, L["plan"], L["y"], L["gates"], L["out"])
+    torch.cuda.synchronize()
+
+    def layer_bwd_head(L):
+        mx.moe_combine_backward(c, L["plan"], L["dout"], L["y"], L["gates"], path.dy_b,
+                                path.dgates)
+        mx.moe_grouped_gemm_dgrad(c, path.dy_b, L["w"], w_pool, L["plan"].cu_seqlens,
+                                  path.dxperm, 0, s.R, ws)
+
+    def layer_bwd_tail(L):
+        mx.moe_grouped_gemm_wgrad(c, L["plan"], L["xperm"], path.dy_b, L["gh"], g_pool, ws)
+        mx.moe_reduce_grad(c, L["plan"], L["gh"], g_pool)
+        mx.moe_dispatch_backward(c, L["plan"], path.dxperm, path.dx)
+
+    def backward(overlap):
+        layer_bwd_head(L1)
+        if overlap:
+            released, filled = torch.cuda.Event(), torch.cuda.Event()
+            released.record(compute)
+            copy.wait_event(released)
+            mx.moe_prefetch_weight(c, L0["plan"], L0["w"], w_pool, stream=copy)
+            filled.record(copy)
+            layer_bwd_tail(L1)
+            compute.wait_event(filled)
+        else:
+            layer_bwd_tail(L1)
+            mx.moe_prefetch_weight(c, L0["plan"], L0["w"], w_pool)
+        layer_bwd_head(L0)
+        layer_bwd_tail(L0)
+
+    out = {"workload": "two layers of one projection at the bench shape sharing one slot buffer "
+                       "[R*B, 7168, 2048] bf16 and one reduce buffer (fp32): 33.8 GB in all, "
+                       "instead of 33.8 GB per layer; layer 0 Theorem-2 routing, layer 1 the "
+                       "step's routing; backward of both layers"}
+    sv = {k: L["plan"].views()["slot_expert"].cpu().numpy() for k, L in (("layer0", L0),
+                                                                         ("layer1", L1))}
+    out["slots"] = {k: int((v >= 0).sum()) for k, v in sv.items()}
+    out["reprefetch_GB"] = 4.0 * s.H * s.Hp * out["slots"]["layer0"] / 1e9
+    for name, overlap in (("serialized", False), ("overlapped", True), ("serialized_2", False),
+                          ("overlapped_2", True)):
+        ts = []
+        for _ in range(reps + 1):
+            mx.moe_prefetch_weight(c, L1["plan"], L1["w"], w_pool)    # pool back to layer 1
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(compute)
+            backward(overlap)
+            b.record(compute)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[name + "_ms"] = float(np.mean(ts[1:]))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(compute)
+    mx.moe_prefetch_weight(c, L0["plan"], L0["w"], w_pool)
+    b.record(compute)
+    torch.cuda.synchronize()
+    out["reprefetch_alone_ms"] = a.elapsed_time(b)
+    ser = (out["serialized_ms"] + out["serialized_2_ms"]) / 2
+    ovl = (out["overlapped_ms"] + out["overlapped_2_ms"]) / 2
+    out["hidden_ms"] = ser - ovl
+    # leave the step's buffers as they were: the pool holds layer 1's slots
+    mx.moe_prefetch_weight(c, L1["plan"], L1["w"], w_pool)
+    del L0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_backward(path, steps, warmup):
     path.run(warmup, timed=False, backward=True)
     torch.cuda.synchronize()
@@ -708,6 +817,8 @@ def main():
     line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
     log("swiglu expert")
     line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
+    log("prefetch pool (two layers, backward)")
+    line["prefetch_pool"] = measure_pool(path, 2)
     if args.sweep:
         sweep = {}
         for t in W.MAXVIO_SWEEP["bench"]:

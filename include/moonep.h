@@ -30,6 +30,19 @@
  *                            act = silu(gate) * up
  *   moe_swiglu_backward      gradients of the activation
  *
+ * Prefetch pool ("Moonshot AI 开源 MoonEP", 核心思想: the prefetch slots come
+ * from one rank-global pool shared by all layers, so the extra memory is B
+ * expert weights per projection in total, not per layer).  w_pref and
+ * grad_pref may be one buffer per projection shared by every layer; a slot
+ * is only read when the current plan puts an expert in it, and reduce_grad
+ * consumes what the weight gradient wrote, so stale contents never matter.
+ * The caller keeps three orders (one stream keeps them all): a layer's
+ * moe_prefetch_weight after the previous user's last moe_grouped_gemm /
+ * moe_grouped_gemm_dgrad of the slots; in the backward, each layer's own
+ * moe_prefetch_weight again before its moe_grouped_gemm_dgrad (the pool
+ * holds another layer's experts); a layer's moe_grouped_gemm_wgrad after
+ * the previous layer's moe_reduce_grad.
+ *
  * Every projection of an expert is its own [E+B, H_in, H_out] weight view;
  * the GEMM, prefetch, wgrad, dgrad, combine and reduce_grad entry points take
  * the projection's widths as cfg->H (input) and cfg->Hp (output), so a down
