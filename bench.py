@@ -20,7 +20,7 @@ and a two-layer backward sharing one prefetch pool ("prefetch_pool").
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
-                    [--sweep] [--no-cpu-baseline]
+                    [--sweep] [--no-cpu-baseline] [--no-extras] [--swiglu-only]
 """
 import argparse
 import json
@@ -672,6 +672,12 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time plan/dispatch/gemm/combine "
                     "at every maxvio of the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the SwiGLU-expert and prefetch-pool blocks (they launch k_gemm<0>, "
+                         "k_prefetch and k_reduce_grad at other shapes; profiles of the step "
+                         "use this)")
+    ap.add_argument("--swiglu-only", action="store_true",
+                    help="plan and dispatch once, then only the SwiGLU-expert block")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                           "CMD_FETCH", "CMD_WRITE"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs and exit")
@@ -712,6 +718,12 @@ def main():
     log("allocating and generating inputs")
     path = Path(shape, ids, gates)
     torch.cuda.synchronize()
+    if args.swiglu_only:
+        path.run(1, timed=False, only=("plan", "dispatch"))
+        torch.cuda.synchronize()
+        print(json.dumps({"swiglu_expert": measure_swiglu(path, max(3, args.steps // 4))}),
+              flush=True)
+        return
     log("warmup + timed steps")
     ms, span_ms, wall_ms = measure(path, args.steps, args.warmup)
     st = path.plan.views()["status"].cpu().numpy()
@@ -815,10 +827,11 @@ def main():
     line["data_backward"] = bwd
     log("dedup dispatch")
     line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
-    log("swiglu expert")
-    line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
-    log("prefetch pool (two layers, backward)")
-    line["prefetch_pool"] = measure_pool(path, 2)
+    if not args.no_extras:
+        log("swiglu expert")
+        line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
+        log("prefetch pool (two layers, backward)")
+        line["prefetch_pool"] = measure_pool(path, 2)
     if args.sweep:
         sweep = {}
         for t in W.MAXVIO_SWEEP["bench"]:
