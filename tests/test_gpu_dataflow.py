@@ -142,7 +142,10 @@ def test_gemm_rank_range_leaves_other_ranks():
     (W.TINY.with_(H=72, Hp=40, S=37), "uniform", 1),
     (W.TINY.with_(R=2, E=4, S=300, K=2, B=2, H=136, Hp=264), "hot", 0),
     (W.SKEWED.with_(H=256, Hp=256), "zipf", 10.0),
-    (W.SKEWED.with_(H=256, Hp=128, name="skewed_adv"), "theorem2", 0)],
+    (W.SKEWED.with_(H=256, Hp=128, name="skewed_adv"), "theorem2", 0),
+    # 12 tiles per item: the per-XCD chunks of the weight gradient start
+    # inside items
+    (W.SKEWED.with_(H=520, Hp=776, name="skewed_wide"), "zipf", 10.0)],
     ids=lambda v: str(getattr(v, "name", v)))
 def test_backward_path(shape, kind, arg):
     announce("backward", shape, kind, arg)
