@@ -16,7 +16,9 @@ the same way and reported beside the step ("data_backward"), outside
 `value`, and so are the two-projection SwiGLU expert's kernels at the same
 shape ("swiglu_expert": first projection [E+B, 7168, 2*2048] fused with
 the activation, second projection [E+B, 2048, 7168], activation backward),
-and a two-layer backward sharing one prefetch pool ("prefetch_pool").
+a two-layer backward sharing one prefetch pool ("prefetch_pool"), and the
+Large-E shape (R=64, S=4096, E=896, K=16): plan, dispatch and combine over
+all 64 ranks and one rank's grouped GEMM ("large_e").
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
@@ -624,6 +626,85 @@ def measure_pool(path, reps):
     return out
 
 
+def measure_large_e(reps):
+    """The Large-E shape: R=64 virtual ranks, S=4096, E=896, K=16, H=7168,
+    H'=2048, B=14, train mode, zipf maxvio 1 and 10.
+
+    Plan, dispatch and combine run over all 64 ranks; the grouped GEMM of
+    one rank -- the one with the most active segments (ties: lowest id), and
+    rank 0 -- against its [910, 7168, 2048] view (896 home rows + its 14
+    prefetch rows).  Each call is timed with HIP events, mean of ``reps``
+    calls after one warm-up.
+    """
+    s, dev = W.LARGE_E, "cuda"
+    c = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    rows = s.R * s.SK
+    x = W.randn_bf16((s.tokens, s.H), 31, dev)
+    w_home = W.randn_bf16((s.E, s.H, s.Hp), 32, dev, chunk_rows=1)
+    w_pref = torch.empty((s.R * s.B, s.H, s.Hp), **bf)
+    xperm = torch.empty((rows, s.H), **bf)
+    y = W.randn_bf16((rows, s.Hp), 33, dev)
+    out = torch.empty((s.tokens, s.Hp), **bf)
+    ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device=dev)
+    plan = mx.Plan(c, dev)
+    T = s.tokens
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.mean(ts))
+
+    res = {"workload": "Large-E: R=64 virtual ranks, S=4096 tokens/rank, E=896, K=16, H=7168, "
+                       "H'=2048, B=14, train mode; plan/dispatch/combine over all ranks, grouped "
+                       "GEMM of one rank's 65536 rows against its [910, 7168, 2048] view"}
+    disp_b = T * (2.0 * s.H * (1 + s.K) + 4 * s.K)
+    comb_b = T * (2.0 * s.Hp * (s.K + 1) + 8 * s.K)
+    flop = 2.0 * s.H * s.Hp * s.SK
+    for t in W.MAXVIO_SWEEP["large_e"]:
+        ids, gates, _, mv = W.routing_zipf(s, t)
+        ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
+        g_t = torch.from_numpy(np.ascontiguousarray(gates, np.float32)).to(dev)
+        r_plan = plan_latency(s, t, ids=ids)
+        mx.moe_plan_run_policy(c, ids_t, plan, PLAN_POLICY)
+        mx.moe_prefetch_weight(c, plan, w_home, w_pref)
+        torch.cuda.synchronize()
+        seg = np.diff(plan.views()["cu_seqlens"].cpu().numpy(), axis=1)
+        active = (seg > 0).sum(axis=1)
+        r_hot = int(np.argmax(active))
+        ms_d = timed(lambda: mx.moe_dispatch(c, plan, x, xperm))
+        ms_c = timed(lambda: mx.moe_combine(c, plan, y, g_t, out))
+        ms_g = timed(lambda: mx.moe_grouped_gemm(c, xperm, w_home, w_pref, plan.cu_seqlens, y,
+                                                 r_hot, r_hot + 1, ws))
+        ms_g0 = timed(lambda: mx.moe_grouped_gemm(c, xperm, w_home, w_pref, plan.cu_seqlens, y,
+                                                  0, 1, ws))
+        res["maxvio_%g" % t] = {
+            "maxvio": mv, "plan_us": r_plan["plan_us_median"],
+            "max_redundant": r_plan["max_redundant"],
+            "dispatch_ms": ms_d, "dispatch_GBps": disp_b / ms_d / 1e6,
+            "dispatch_frac": disp_b / ms_d / 1e6 / HBM_PEAK_GBPS,
+            "combine_ms": ms_c, "combine_GBps": comb_b / ms_c / 1e6,
+            "combine_frac": comb_b / ms_c / 1e6 / HBM_PEAK_GBPS,
+            "gemm_rank": r_hot, "gemm_rank_active_segments": int(active[r_hot]),
+            "gemm_ms": ms_g, "gemm_TFLOPs": flop / ms_g / 1e9,
+            "gemm_frac": flop / ms_g / 1e9 / BF16_PEAK_TFLOPS,
+            "gemm_rank0_ms": ms_g0, "gemm_rank0_TFLOPs": flop / ms_g0 / 1e9}
+        log("large_e", t, res["maxvio_%g" % t])
+    del x, w_home, w_pref, xperm, y, out, ws, plan
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_backward(path, steps, warmup):
     path.run(warmup, timed=False, backward=True)
     torch.cuda.synchronize()
@@ -851,6 +932,12 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host, bounded sample)")
         line["cpu_baseline"] = cpu_baseline(shape, ids, gates, path)
+    if not args.no_extras:
+        log("large-E shape (the step's buffers released first)")
+        del path
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        line["large_e"] = measure_large_e(5)
     print(json.dumps(line), flush=True)
 
 
