@@ -16,7 +16,9 @@ the same way and reported beside the step ("data_backward"), outside
 `value`, and so are the two-projection SwiGLU expert's kernels at the same
 shape ("swiglu_expert": first projection [E+B, 7168, 2*2048] fused with
 the activation, second projection [E+B, 2048, 7168], activation backward),
-a two-layer backward sharing one prefetch pool ("prefetch_pool"), and the
+a two-layer backward sharing one prefetch pool ("prefetch_pool"), the
+Theorem-2 worst case at the same shape, training and inference B=4
+("theorem2"), and the
 Large-E shape (R=64, S=4096, E=896, K=16): plan, dispatch and combine over
 all 64 ranks and one rank's grouped GEMM ("large_e").
 Prints one JSON line.
@@ -403,6 +405,67 @@ def measure(path, steps, warmup):
     ms = {n: float(np.mean(v)) for n, v in per.items() if v}
     span = ev[0][0][1].elapsed_time(ev[-1][-1][2])
     return ms, span / steps, wall / steps * 1e3
+
+
+def measure_theorem2(path, steps):
+    """The Theorem-2 worst case at the bench shape (round-robin routing over
+    the experts of ranks 1..7, gates 1/K): the training step with B = 48
+    (rank 0 receives 42 experts from one donor, 168 slots in all), and the
+    inference forward with B = 4 (four slots per rank, the other redundant
+    experts read from their home rows).  Restores the step's routing and plan
+    afterwards.
+    """
+    s, dev = path.shape, "cuda"
+    saved = (path.ids, path.gates)
+    path.ids = torch.from_numpy(np.ascontiguousarray(W.routing_theorem2(s), np.int32)).to(dev)
+    path.gates = torch.from_numpy(W.gates_uniform(s)).to(dev)
+    ms, span, _ = measure(path, steps, 1)
+    units, stats = work_units(s, path.plan.views())
+    nred = path.plan.views()["n_redundant"].cpu().numpy().tolist()
+    out = {"workload": "bench shape, Theorem-2 routing (slot i -> expert E/R + i mod (E - E/R)), "
+                       "gates 1/K",
+           "train": {"n_redundant": nred, "slots": stats["slots"], "step_ms": span,
+                     "ms": ms,
+                     "prefetch_GB": units["prefetch"][1] / 1e9,
+                     "prefetch_GBps": units["prefetch"][1] / ms["prefetch"] / 1e6,
+                     "reduce_grad_GB": units["reduce_grad"][1] / 1e9,
+                     "reduce_grad_GBps": units["reduce_grad"][1] / ms["reduce_grad"] / 1e6,
+                     "gemm_TFLOPs": units["gemm"][1] / ms["gemm"] / 1e9,
+                     "wgrad_TFLOPs": units["wgrad"][1] / ms["wgrad"] / 1e9}}
+    # inference, B = 4: the step's buffers with a 4-slot view of w_pref
+    ci = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, 4, mx.MODE_INFER)
+    pi = mx.Plan(ci, dev)
+    wpi = path.w_pref[:s.R * 4]
+    calls = (("plan", lambda: mx.moe_plan_run_policy(ci, path.ids, pi, PLAN_POLICY)),
+             ("prefetch", lambda: mx.moe_prefetch_weight(ci, pi, path.w_home, wpi)),
+             ("dispatch", lambda: mx.moe_dispatch(ci, pi, path.x, path.xperm)),
+             ("gemm", lambda: mx.moe_grouped_gemm(ci, path.xperm, path.w_home, wpi,
+                                                  pi.cu_seqlens, path.y, 0, s.R, path.ws)),
+             ("combine", lambda: mx.moe_combine(ci, pi, path.y, path.gates, path.out)))
+    for _, f in calls:
+        f()
+    torch.cuda.synchronize()
+    ts = {n: [] for n, _ in calls}
+    for _ in range(steps):
+        for n, f in calls:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts[n].append(a.elapsed_time(b))
+    v = pi.views()
+    out["inference_B4"] = {
+        "ms": {n: float(np.mean(t)) for n, t in ts.items()},
+        "n_redundant": v["n_redundant"].cpu().numpy().tolist(),
+        "gemm_TFLOPs": units["gemm"][1] / float(np.mean(ts["gemm"])) / 1e9}
+    path.ids, path.gates = saved
+    mx.moe_plan_run_policy(path.c, path.ids, path.plan, PLAN_POLICY)
+    mx.moe_prefetch_weight(path.c, path.plan, path.w_home, path.w_pref)
+    mx.moe_dispatch(path.c, path.plan, path.x, path.xperm)
+    torch.cuda.synchronize()
+    return out
 
 
 def measure_dedup(path, steps):
@@ -909,6 +972,8 @@ def main():
     log("dedup dispatch")
     line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
     if not args.no_extras:
+        log("theorem-2 worst case (train B=48, inference B=4)")
+        line["theorem2"] = measure_theorem2(path, max(3, args.steps // 4))
         log("swiglu expert")
         line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
         log("prefetch pool (two layers, backward)")
