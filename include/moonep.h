@@ -65,6 +65,9 @@
  *  - conditions only the device can see (expert ids outside [0, E)) set bits
  *    in plan->status instead, and every later step of that plan then leaves
  *    its outputs untouched where the route is -1;
+ *  - every bf16 and fp32 tensor argument (and every `workspace`) starts on a
+ *    16-byte boundary (the kernels move 16-byte vectors); a misaligned base
+ *    is MOE_EINVAL.  torch and hipMalloc allocations are 256-byte aligned;
  *  - bf16 tensors are raw IEEE bfloat16 bit patterns (moe_bf16); rounding to
  *    bf16 is round-to-nearest-even; all arrays are dense row-major.
  *
@@ -373,8 +376,7 @@ int moe_grouped_gemm_swiglu(const moe_cfg *cfg, const moe_bf16 *xperm,
  *   dh13[:, :H'] = bf16( dact * up * s * (1 + gate * (1 - s)) )   (d gate)
  *   dh13[:, H':] = bf16( dact * gate * s )                        (d up)
  * h13, dh13 [R][S*K][2H'] bf16, dact [R][S*K][H'] bf16.  dh13 may be h13
- * (in place); it must not overlap dact otherwise.  All three 16-byte aligned
- * (else MOE_EINVAL).
+ * (in place); it must not overlap dact otherwise.
  */
 int moe_swiglu_backward(const moe_cfg *cfg, const moe_bf16 *h13, const moe_bf16 *dact,
                         moe_bf16 *dh13, hipStream_t stream);

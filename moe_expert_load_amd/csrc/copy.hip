@@ -386,6 +386,7 @@ extern "C" int moe_prefetch_weight(const moe_cfg* cfg, const moe_plan* plan,
   const int64_t RB = int64_t(cfg->R) * cfg->B;
   if (RB == 0) return MOE_OK;
   if (!w_home || !w_pref) return MOE_EINVAL;
+  if (!aligned16(w_home, w_pref)) return MOE_EINVAL;
   const int64_t nvec = int64_t(cfg->H) * cfg->Hp / 8;
   int chunks = (int)std::min<int64_t>(64, (nvec + 256 * 16 - 1) / (256 * 16));
   if (chunks < 1) chunks = 1;
@@ -402,6 +403,7 @@ extern "C" int moe_dispatch(const moe_cfg* cfg, const moe_plan* plan, const moe_
   const int ntok = cfg->R * cfg->S;
   if (ntok == 0) return MOE_OK;
   if (!plan || !plan->route || !x || !xperm) return MOE_EINVAL;
+  if (!aligned16(x, xperm)) return MOE_EINVAL;
   const int hv = cfg->H / 8;
   const int q = (hv + 4 * kWave - 1) / (4 * kWave);   // vectors per lane for one pass
   const dim3 grid(ntok), block(256);
@@ -435,6 +437,7 @@ extern "C" int moe_dispatch_dedup(const moe_cfg* cfg, const int32_t* route_enc, 
   const int ntok = cfg->R * cfg->S;
   if (ntok == 0) return MOE_OK;
   if (!route_enc || !x || !xperm) return MOE_EINVAL;
+  if (!aligned16(x, xperm)) return MOE_EINVAL;
   const int hv = cfg->H / 8;
   const int du = (hv + kWave - 1) / kWave;
   const dim3 grid((ntok + 3) / 4), block(256);
@@ -461,6 +464,7 @@ extern "C" int moe_combine(const moe_cfg* cfg, const moe_plan* plan, const moe_b
   const int ntok = cfg->R * cfg->S;
   if (ntok == 0) return MOE_OK;
   if (!plan || !plan->route || !y || !gates || !out) return MOE_EINVAL;
+  if (!aligned16(y, out)) return MOE_EINVAL;
   const int hv = cfg->Hp / 8;
   const int cu = (hv + kWave - 1) / kWave;
   const dim3 grid((ntok + 3) / 4), block(256);
@@ -484,6 +488,7 @@ extern "C" int moe_combine_backward(const moe_cfg* cfg, const moe_plan* plan, co
   const int ntok = cfg->R * cfg->S;
   if (ntok == 0) return MOE_OK;
   if (!plan || !plan->route || !dout || !y || !gates || !dy || !dgates) return MOE_EINVAL;
+  if (!aligned16(dout, y, dy)) return MOE_EINVAL;
   const int hv = cfg->Hp / 8;
   const int cu = (hv + kWave - 1) / kWave;
   const dim3 grid((ntok + 3) / 4), block(256);
@@ -507,6 +512,7 @@ extern "C" int moe_dispatch_backward(const moe_cfg* cfg, const moe_plan* plan,
   const int ntok = cfg->R * cfg->S;
   if (ntok == 0) return MOE_OK;
   if (!plan || !plan->route || !dxperm || !dx) return MOE_EINVAL;
+  if (!aligned16(dxperm, dx)) return MOE_EINVAL;
   const int hv = cfg->H / 8;
   const int cu = (hv + kWave - 1) / kWave;
   const dim3 grid((ntok + 3) / 4), block(256);
@@ -529,6 +535,7 @@ extern "C" int moe_reduce_grad(const moe_cfg* cfg, const moe_plan* plan, float* 
   if (!plan || !plan->workspace) return MOE_EINVAL;
   if (cfg->B == 0) return MOE_OK;
   if (!grad_home || !grad_pref) return MOE_EINVAL;
+  if (!aligned16(grad_home, grad_pref)) return MOE_EINVAL;
   if ((int64_t(cfg->H) * cfg->Hp) % 4 != 0) return MOE_EINVAL;
   const PlanLayout L = plan_layout(cfg);
   void* ws = plan->workspace;

@@ -979,6 +979,7 @@ extern "C" int moe_grouped_gemm(const moe_cfg* cfg, const moe_bf16* xperm, const
   if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
   if (!xperm || !w_home || !cu_seqlens || !y || !workspace) return MOE_EINVAL;
   if (cfg->B > 0 && !w_pref) return MOE_EINVAL;
+  if (!aligned16(xperm, w_home, w_pref, y, workspace)) return MOE_EINVAL;
   GemmArgs g{};
   g.xperm = xperm; g.w_home = w_home; g.w_pref = w_pref; g.y = y;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
@@ -1007,6 +1008,7 @@ extern "C" int moe_grouped_gemm_swiglu(const moe_cfg* cfg, const moe_bf16* xperm
   if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
   if (!xperm || !w13_home || !cu_seqlens || !act || !workspace) return MOE_EINVAL;
   if (cfg->B > 0 && !w13_pref) return MOE_EINVAL;
+  if (!aligned16(xperm, w13_home, w13_pref, act, h13, workspace)) return MOE_EINVAL;
   GemmArgs g{};
   g.xperm = xperm; g.w_home = w13_home; g.w_pref = w13_pref; g.y = act; g.h13 = h13;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
@@ -1032,6 +1034,7 @@ extern "C" int moe_grouped_gemm_dgrad(const moe_cfg* cfg, const moe_bf16* dy, co
   if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
   if (!dy || !w_home || !cu_seqlens || !dxperm || !workspace) return MOE_EINVAL;
   if (cfg->B > 0 && !w_pref) return MOE_EINVAL;
+  if (!aligned16(dy, w_home, w_pref, dxperm, workspace)) return MOE_EINVAL;
   GemmArgs g{};
   g.dy = dy; g.w_home = w_home; g.w_pref = w_pref; g.y = dxperm;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
@@ -1055,6 +1058,7 @@ extern "C" int moe_grouped_gemm_wgrad(const moe_cfg* cfg, const moe_plan* plan,
   if (cfg->mode != MOE_MODE_TRAIN) return MOE_EINVAL;
   if (!plan || !plan->cu_seqlens || !xperm || !dy || !grad_home || !workspace) return MOE_EINVAL;
   if (cfg->B > 0 && !grad_pref) return MOE_EINVAL;
+  if (!aligned16(xperm, dy, grad_home, grad_pref, workspace)) return MOE_EINVAL;
   GemmArgs g{};
   g.xperm = xperm; g.dy = dy; g.grad_home = grad_home; g.grad_pref = grad_pref;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;

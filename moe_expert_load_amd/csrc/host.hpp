@@ -34,6 +34,14 @@ inline int check_cfg(const moe_cfg* c) {
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// Every bf16 / fp32 tensor is moved in 16-byte vectors (and the GEMMs load
+// 16 bytes per lane straight into LDS), so tensor bases must be 16-byte
+// aligned.  A null pointer passes (null checks are separate).
+template <typename... P>
+inline bool aligned16(const P*... p) {
+  return (((reinterpret_cast<uintptr_t>(p) & 15) == 0) && ...);
+}
+
 // Plan scratch: chunk counts and the per-expert tables k_route reads.
 struct PlanLayout {
   int64_t N;      // R*S*K slots

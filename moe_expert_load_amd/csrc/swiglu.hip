@@ -82,7 +82,7 @@ extern "C" int moe_swiglu_backward(const moe_cfg* cfg, const moe_bf16* h13, cons
   const uintptr_t h0 = reinterpret_cast<uintptr_t>(h13);
   if (o0 < d1 && d0 < o1) return MOE_EINVAL;
   if (dh13 != h13 && o0 < h0 + (o1 - o0) && h0 < o1) return MOE_EINVAL;
-  if ((o0 | d0 | h0) & 15) return MOE_EINVAL;    // 16-byte pieces
+  if (!aligned16(h13, dact, dh13)) return MOE_EINVAL;
   const int64_t pairs = (rows + 1) / 2;
   const int64_t grid = pairs < 4096 ? pairs : 4096;
   hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)grid), dim3(kSwiThreads), 0, stream,

@@ -100,6 +100,23 @@ def test_host_only_calls_and_validation():
     assert lib.moe_swiglu_backward(ctypes.byref(small), ctypes.c_void_p((1 << 30) + 8),
                                    ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28),
                                    None) == mx.MOE_EINVAL
+    # tensor bases off a 16-byte boundary are rejected before any launch
+    A, M = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    fake = mx.moe_plan(*[ctypes.c_void_p(1 << 24) for _ in mx.PLAN_FIELDS])
+    assert lib.moe_dispatch(ctypes.byref(small), ctypes.byref(fake), M, A, None) == mx.MOE_EINVAL
+    assert lib.moe_combine(ctypes.byref(small), ctypes.byref(fake), A, A, M, None) == mx.MOE_EINVAL
+    assert lib.moe_prefetch_weight(ctypes.byref(small), ctypes.byref(fake), A, M,
+                                   None) == mx.MOE_EINVAL
+    assert lib.moe_grouped_gemm(ctypes.byref(small), M, A, A, A, A, 0, 4, A,
+                                None) == mx.MOE_EINVAL
+    assert lib.moe_grouped_gemm_dgrad(ctypes.byref(small), A, A, A, A, M, 0, 4, A,
+                                      None) == mx.MOE_EINVAL
+    assert lib.moe_grouped_gemm_wgrad(ctypes.byref(small), ctypes.byref(fake), A, A, M, A, A,
+                                      None) == mx.MOE_EINVAL
+    assert lib.moe_grouped_gemm_swiglu(ctypes.byref(small), A, A, A, A, A, M, 0, 4, A,
+                                       None) == mx.MOE_EINVAL
+    assert lib.moe_reduce_grad(ctypes.byref(small), ctypes.byref(fake), A, M,
+                               None) == mx.MOE_EINVAL
     assert mx.moe_strerror(mx.MOE_EINVAL).startswith("invalid")
     assert mx.moe_strerror(12345) == "unknown error code"
 
