@@ -914,15 +914,14 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
   if (tid == 0) *s.nitems = min(s_carry, s.cap);
 }
 
-static int g_num_cus = 0;
-
+// Compute units of the current device: the persistent grid's size.  The
+// attribute query is cheap and asked on every launch, so nothing is cached
+// across calls (or devices).
 static int num_cus() {
-  if (g_num_cus > 0) return g_num_cus;
   int dev = 0, v = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
     v = 256;
-  g_num_cus = v;
   return v;
 }
 
