@@ -689,6 +689,57 @@ def measure_pool(path, reps):
     return out
 
 
+def measure_small(reps):
+    """The tiny (R=4, S=16, E=8, K=2, H=128, H'=64) and skewed (R=8, S=1024,
+    E=64, K=4, H=1024, H'=512; zipf maxvio 0.2 / 1 / 10 / 15) shapes: the
+    forward path's calls in microseconds.  Their working sets fit in the
+    256 MB memory-side cache, so no HBM fraction is claimed.
+    """
+    dev = "cuda"
+    out = {"note": "working sets fit in the memory-side cache: times only, no HBM fraction"}
+    cases = [(W.TINY, None)] + [(W.SKEWED, t) for t in W.MAXVIO_SWEEP["skewed"]]
+    for s, t in cases:
+        c = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
+        if t is None:
+            ids, gates = W.routing_uniform(s)
+            name = "tiny"
+        else:
+            ids, gates, _, _ = W.routing_zipf(s, t)
+            name = "skewed_maxvio_%g" % t
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
+        g_t = torch.from_numpy(np.ascontiguousarray(gates, np.float32)).to(dev)
+        plan = mx.Plan(c, dev)
+        x = W.randn_bf16((s.tokens, s.H), 41, dev)
+        w = W.randn_bf16((s.E, s.H, s.Hp), 42, dev)
+        wp = torch.empty((max(1, s.R * s.B), s.H, s.Hp), **bf)
+        xp = torch.empty((s.R * s.SK, s.H), **bf)
+        y = torch.empty((s.R * s.SK, s.Hp), **bf)
+        o = torch.empty((s.tokens, s.Hp), **bf)
+        ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device=dev)
+        calls = (("plan", lambda: mx.moe_plan_run_policy(c, ids_t, plan, PLAN_POLICY)),
+                 ("prefetch", lambda: mx.moe_prefetch_weight(c, plan, w, wp)),
+                 ("dispatch", lambda: mx.moe_dispatch(c, plan, x, xp)),
+                 ("gemm", lambda: mx.moe_grouped_gemm(c, xp, w, wp, plan.cu_seqlens, y, 0, s.R,
+                                                      ws)),
+                 ("combine", lambda: mx.moe_combine(c, plan, y, g_t, o)))
+        for _, f in calls:
+            f()
+        torch.cuda.synchronize()
+        ts = {n: [] for n, _ in calls}
+        for _ in range(reps):
+            for n, f in calls:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                f()
+                b.record()
+                torch.cuda.synchronize()
+                ts[n].append(a.elapsed_time(b) * 1e3)
+        out[name] = {n + "_us": float(np.median(v)) for n, v in ts.items()}
+    return out
+
+
 def measure_large_e(reps):
     """The Large-E shape: R=64 virtual ranks, S=4096, E=896, K=16, H=7168,
     H'=2048, B=14, train mode, zipf maxvio 1 and 10.
@@ -972,6 +1023,8 @@ def main():
     log("dedup dispatch")
     line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
     if not args.no_extras:
+        log("tiny and skewed shapes")
+        line["small_shapes"] = measure_small(10)
         log("theorem-2 worst case (train B=48, inference B=4)")
         line["theorem2"] = measure_theorem2(path, max(3, args.steps // 4))
         log("swiglu expert")
