@@ -689,6 +689,68 @@ def measure_pool(path, reps):
     return out
 
 
+def _time_calls(f, reps):
+    f()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        f()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def measure_graph(path, reps):
+    """The step captured once as a HIP graph (static shapes, no host sync in
+    any call) and replayed, against the same calls issued eagerly: at the
+    bench shape (the whole training step) and at the tiny and skewed shapes
+    (plan -> prefetch -> dispatch -> GEMM -> combine), where launches weigh
+    most.  Median of ``reps`` after a warm-up.
+    """
+    out = {}
+    step = lambda: path.run(1, timed=False)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    out["bench_step"] = {"eager_ms": _time_calls(step, reps), "graph_ms": _time_calls(g.replay, reps)}
+    dev = "cuda"
+    for s, t in ((W.TINY, None), (W.SKEWED, 1.0)):
+        c = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
+        ids, gates = W.routing_uniform(s) if t is None else W.routing_zipf(s, t)[:2]
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
+        g_t = torch.from_numpy(np.ascontiguousarray(gates, np.float32)).to(dev)
+        plan = mx.Plan(c, dev)
+        x, w = W.randn_bf16((s.tokens, s.H), 41, dev), W.randn_bf16((s.E, s.H, s.Hp), 42, dev)
+        wp = torch.empty((s.R * s.B, s.H, s.Hp), **bf)
+        xp, y = torch.empty((s.R * s.SK, s.H), **bf), torch.empty((s.R * s.SK, s.Hp), **bf)
+        o = torch.empty((s.tokens, s.Hp), **bf)
+        ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            mx.moe_plan_run_policy(c, ids_t, plan, PLAN_POLICY)
+            mx.moe_prefetch_weight(c, plan, w, wp)
+            mx.moe_dispatch(c, plan, x, xp)
+            mx.moe_grouped_gemm(c, xp, w, wp, plan.cu_seqlens, y, 0, s.R, ws)
+            mx.moe_combine(c, plan, y, g_t, o)
+        fwd()
+        torch.cuda.synchronize()
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            fwd()
+        torch.cuda.synchronize()
+        out[s.name + "_forward"] = {"eager_us": _time_calls(fwd, reps) * 1e3,
+                                    "graph_us": _time_calls(gs.replay, reps) * 1e3}
+    return out
+
+
 def measure_small(reps):
     """The tiny (R=4, S=16, E=8, K=2, H=128, H'=64) and skewed (R=8, S=1024,
     E=64, K=4, H=1024, H'=512; zipf maxvio 0.2 / 1 / 10 / 15) shapes: the
@@ -1025,6 +1087,8 @@ def main():
     if not args.no_extras:
         log("tiny and skewed shapes")
         line["small_shapes"] = measure_small(10)
+        log("graph capture and replay")
+        line["graph_replay"] = measure_graph(path, 10)
         log("theorem-2 worst case (train B=48, inference B=4)")
         line["theorem2"] = measure_theorem2(path, max(3, args.steps // 4))
         log("swiglu expert")
