@@ -274,3 +274,37 @@ def test_bench_shape_swiglu():
     torch.cuda.synchronize()
     hb, db = bits(h13.index_select(0, idx)), bits(dact.index_select(0, idx))
     swiglu_bwd_close(bits(dh13.index_select(0, idx)), swiglu.swiglu_backward(hb, db), hb, db)
+
+
+def test_swiglu_gemm_rank_range_leaves_other_ranks():
+    shape = W.SKEWED.with_(H=256, Hp=128)
+    c, oc = cfgs(shape)
+    c13, _ = proj_cfgs(shape, shape.H, 2 * shape.Hp)
+    ids, _, _, _ = W.routing_zipf(shape, 10.0)
+    ref = make_plan(ids, oc)
+    plan, _ = gpu_plan(shape, ids)
+    announce("swiglu rank range 2..6")
+    x = W.randn_bf16((shape.tokens, shape.H), 91, "cuda")
+    w13 = W.randn_bf16((shape.E, shape.H, 2 * shape.Hp), 92, "cuda")
+    w13p = torch.zeros((shape.R * shape.B, shape.H, 2 * shape.Hp), dtype=torch.bfloat16,
+                       device="cuda")
+    rows = shape.R * shape.SK
+    xp = torch.empty((rows, shape.H), dtype=torch.bfloat16, device="cuda")
+    act, h13 = sentinel(rows, shape.Hp), sentinel(rows, 2 * shape.Hp)
+    ws = torch.empty(mx.moe_gemm_workspace_size(c13), dtype=torch.uint8, device="cuda")
+    mx.moe_prefetch_weight(c13, plan, w13, w13p)
+    mx.moe_dispatch(c, plan, x, xp)
+    mx.moe_grouped_gemm_swiglu(c, xp, w13, w13p, plan.cu_seqlens, act, h13, 2, 6, ws)
+    torch.cuda.synchronize()
+    wb = bits(w13)
+    ref_act, ref_h13 = swiglu.swiglu_gemm(dataflow.dispatch(bits(x), ref, oc), wb,
+                                          dataflow.prefetch(wb, ref, oc), ref, oc,
+                                          ranks=[2, 3, 4, 5])
+    SK = shape.SK
+    ga, gh = bits(act), bits(h13)
+    rows_close(ga[2 * SK:6 * SK], ref_act[2 * SK:6 * SK])
+    rows_close(gh[2 * SK:6 * SK], ref_h13[2 * SK:6 * SK])
+    for g in (ga, gh):
+        assert np.all(g[:2 * SK] == SENT) and np.all(g[6 * SK:] == SENT)
+    with pytest.raises(mx.MoeError):
+        mx.moe_grouped_gemm_swiglu(c, xp, w13, w13p, plan.cu_seqlens, act, h13, 6, 2, ws)
