@@ -215,8 +215,10 @@ int moe_dispatch(const moe_cfg *cfg, const moe_plan *plan, const moe_bf16 *x,
                  moe_bf16 *xperm, hipStream_t stream);
 
 /*
- * Host only.  Bytes of scratch that moe_grouped_gemm, moe_grouped_gemm_dgrad
- * and moe_grouped_gemm_wgrad need in their `workspace` argument.
+ * Host only.  Bytes of scratch that moe_grouped_gemm, moe_grouped_gemm_dgrad,
+ * moe_grouped_gemm_wgrad and moe_grouped_gemm_swiglu need in their
+ * `workspace` argument.  The size depends on R, S, K, E and B only, so one
+ * workspace serves every projection of a layer.
  */
 int moe_gemm_workspace_size(const moe_cfg *cfg, size_t *bytes_out);
 
