@@ -403,8 +403,10 @@ def measure(path, steps, warmup):
         for name, a, b in row:
             per[name].append(a.elapsed_time(b))
     ms = {n: float(np.mean(v)) for n, v in per.items() if v}
+    stats = {n: {"mean": float(np.mean(v)), "median": float(np.median(v)),
+                 "min": float(np.min(v))} for n, v in per.items() if v}
     span = ev[0][0][1].elapsed_time(ev[-1][-1][2])
-    return ms, span / steps, wall / steps * 1e3
+    return ms, span / steps, wall / steps * 1e3, stats
 
 
 def measure_theorem2(path, steps):
@@ -419,7 +421,7 @@ def measure_theorem2(path, steps):
     saved = (path.ids, path.gates)
     path.ids = torch.from_numpy(np.ascontiguousarray(W.routing_theorem2(s), np.int32)).to(dev)
     path.gates = torch.from_numpy(W.gates_uniform(s)).to(dev)
-    ms, span, _ = measure(path, steps, 1)
+    ms, span, _, _ = measure(path, steps, 1)
     units, stats = work_units(s, path.plan.views())
     nred = path.plan.views()["n_redundant"].cpu().numpy().tolist()
     out = {"workload": "bench shape, Theorem-2 routing (slot i -> expert E/R + i mod (E - E/R)), "
@@ -982,7 +984,7 @@ def main():
               flush=True)
         return
     log("warmup + timed steps")
-    ms, span_ms, wall_ms = measure(path, args.steps, args.warmup)
+    ms, span_ms, wall_ms, step_stats = measure(path, args.steps, args.warmup)
     st = path.plan.views()["status"].cpu().numpy()
     if st[2] != 0:
         raise RuntimeError("plan status bits %d" % st[2])
@@ -1044,6 +1046,7 @@ def main():
                    "redundant_slots": plan_stats["slots"]},
         "components": comps,
         "step_ms": ms,
+        "step_ms_stats": step_stats,
         "wall_ms_per_step": wall_ms,
         "roofline": roofline,
         "rooflines": roof,
@@ -1101,7 +1104,7 @@ def main():
             ids2, gates2, _, mv2 = W.routing_zipf(shape, t)
             path.ids = torch.from_numpy(np.ascontiguousarray(ids2, np.int32)).cuda()
             path.gates = torch.from_numpy(gates2).cuda()
-            m2, _, _ = measure(path, max(3, args.steps // 2), 2)
+            m2, _, _, _ = measure(path, max(3, args.steps // 2), 2)
             u2, st2 = work_units(shape, path.plan.views())
             sweep["%.1f" % t] = {
                 "maxvio": mv2, "plan_us": m2["plan"] * 1e3,
