@@ -222,6 +222,14 @@ __device__ __forceinline__ unsigned char* epilogue_area2(int wv) {
 #endif
 }
 
+// Two fp32 values to a packed bf16 pair (lo in bits 0-15), rounded to
+// nearest even by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // Workgroup barrier that orders this wave's LDS accesses around it but does
 // not wait for outstanding global loads (the direct-to-LDS loads of later
 // stages stay in flight; each wave waits for its own with wait_vm first).
@@ -766,8 +774,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       __syncthreads();
     } else if (MODE != MODE_WGRAD) {
       // Per wave, two passes of 64 rows x 128 columns staged as bf16 in the
-      // wave's own 16 KB stage array (256-byte rows), then whole 16-byte row
-      // chunks to global memory (rows of NOUT columns).
+      // wave's own 16 KB stage array (256-byte rows; pairs of rows converted
+      // by one hardware instruction), then whole 16-byte row chunks to global
+      // memory (rows of NOUT columns).  All LDS reads of a pass are issued
+      // before its stores, so the stores do not wait for one read each.
       unsigned char* Cs = kPair ? (wv < 2 ? g_pa0 : g_pa1) + (wv & 1) * 16384 : epilogue_area(wv);
       uint16_t* yb = g.y + int64_t(it.row0) * NOUT;
 #pragma unroll
@@ -779,24 +789,31 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
           for (int j = 0; j < 4; ++j) {
             const f32x16 a = acc[2 * half + i2][j];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
+            for (int v = 0; v < 16; v += 2) {        // rows mm and mm + 1
               const int mm = 32 * i2 + 8 * (v >> 2) + (v & 3);
-              *reinterpret_cast<uint16_t*>(cbase + mm * 256 + 64 * j) =
-                  (uint16_t)f32_to_bf16(a[v]);
+              const uint32_t p = cvt_pk_bf16(a[v], a[v + 1]);
+              *reinterpret_cast<uint16_t*>(cbase + mm * 256 + 64 * j) = (uint16_t)p;
+              *reinterpret_cast<uint16_t*>(cbase + (mm + 1) * 256 + 64 * j) = (uint16_t)(p >> 16);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
-        for (int c = lane; c < 64 * 16; c += kWave) {
-          const int rr = c >> 4, cc = c & 15;
+        // every LDS read of the pass first, then the stores
+        u32x4 piece[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int c = lane + kWave * k, rr = c >> 4, cc = c & 15;
+          piece[k] = *reinterpret_cast<const u32x4*>(Cs + rr * 256 + cc * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int c = lane + kWave * k, rr = c >> 4, cc = c & 15;
           const int m = wm * 128 + half * 64 + rr;
           const int n = n0 + wn * 128 + cc * 8;
           if (m < it.rows && n < NOUT)
-            *reinterpret_cast<u32x4*>(yb + uint32_t(m) * NOUT + n) =
-                *reinterpret_cast<const u32x4*>(Cs + rr * 256 + cc * 16);
+            *reinterpret_cast<u32x4*>(yb + uint32_t(m) * NOUT + n) = piece[k];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -804,40 +821,30 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       }
       __syncthreads();
     } else {
-      // fp32 gradient rows: per wave, four passes of 32 rows x 128 columns
-      // staged in the wave's own 16 KB stage array (512-byte rows), then
-      // whole 16-byte pieces (a wave writes two 512-byte row pieces per
-      // store) to global memory.
+      // fp32 gradient rows straight from the accumulators: each store
+      // instruction writes two whole 128-byte row pieces (lanes 0-31 and
+      // 32-63, four rows apart).  Full tiles skip the bounds checks.
       float* out = it.j < g.E ? g.grad_home + int64_t(it.j) * H * Hp
                               : g.grad_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
-      unsigned char* Cs = epilogue_area(wv);
+      const int hb0 = m0 + wm * 128 + 4 * (lane >> 5);
+      const int nb0 = n0 + wn * 128 + (lane & 31);
+      auto store_tile = [&](auto full_) {
+        constexpr bool FULL = decltype(full_)::value;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < 4; ++j) {
+            const int n = nb0 + 32 * j;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rr = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            *reinterpret_cast<float*>(Cs + rr * 512 + (32 * j + (lane & 31)) * 4) = acc[i][j][v];
+            for (int v = 0; v < 16; ++v) {
+              const int h = hb0 + 32 * i + 8 * (v >> 2) + (v & 3);
+              if (FULL || (h < H && n < Hp))       // written once: streaming store
+                __builtin_nontemporal_store(acc[i][j][v], out + uint32_t(h) * Hp + n);
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
-        for (int c = lane; c < 32 * 32; c += kWave) {
-          const int rr = c >> 5, cc = c & 31;
-          const int h = m0 + wm * 128 + 32 * i + rr;
-          const int n = n0 + wn * 128 + cc * 4;
-          if (h < H && n < Hp)                     // written once: streaming store
-            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(Cs + rr * 512 + cc * 16),
-                                        reinterpret_cast<f32x4*>(out + uint32_t(h) * Hp + n));
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+      };
+      if (m0 + BM <= H && n0 + BN <= Hp) store_tile(std::true_type());
+      else store_tile(std::false_type());
       __syncthreads();
     }
   }
