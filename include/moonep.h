@@ -198,7 +198,8 @@ int moe_plan_run_policy(const moe_cfg *cfg, const int32_t *topk_ids,
  * prefetch_weight ("Moonshot AI 开源 MoonEP", 核心思想: rows [E, E+B) are local
  * prefetch slots filled by buffer.prefetch_weight).  For every rank r and
  * slot b with slot_expert[r][b] = e >= 0, copies w_home[e] ([H][Hp] bf16)
- * to w_pref[r][b].  Slots holding no expert are not written.
+ * to w_pref[r][b].  Slots holding no expert (or an id outside [0, E)) are not
+ * written.
  * w_home [E][H][Hp], w_pref [R][B][H][Hp]; they must not overlap.
  */
 int moe_prefetch_weight(const moe_cfg *cfg, const moe_plan *plan,

@@ -17,28 +17,67 @@
 namespace moonep {
 
 // ---------------------------------------------------------------------------
-// prefetch: grid (chunks, R*B); slot s = r*B + b copies w_home[slot_expert[s]].
+// prefetch: a fixed grid walks the copies of the slots in use.  Each
+// workgroup first compacts a window of slot entries (slot id and expert)
+// into LDS, in ascending slot order, so every workgroup builds the same list.
+// Each used slot is then cut into CH chunks, chunk c moving vectors
+// c*256 + tid + k*CH*256 (four per step), and the cnt*CH chunks are dealt
+// out over the grid.  CH grows when few slots are used, so the grid stays
+// full either way (a grid of (chunk, slot) pairs over every slot leaves most
+// workgroups idle when a handful of slots hold an expert).
 // ---------------------------------------------------------------------------
+constexpr int kPfWin = 1024;   // slot entries compacted per window
+
 __global__ __launch_bounds__(256) void k_prefetch(const u32x4* __restrict__ w_home,
                                                   u32x4* __restrict__ w_pref,
                                                   const int32_t* __restrict__ slot_expert,
-                                                  int64_t nvec) {
-  const int slot = blockIdx.y;
-  const int e = slot_expert[slot];
-  if (e < 0) return;
-  const u32x4* src = w_home + int64_t(e) * nvec;
-  u32x4* dst = w_pref + int64_t(slot) * nvec;
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; v + 3 * stride < nvec; v += 4 * stride) {
-    const u32x4 a0 = src[v], a1 = src[v + stride], a2 = src[v + 2 * stride],
-                a3 = src[v + 3 * stride];
-    __builtin_nontemporal_store(a0, dst + v);
-    __builtin_nontemporal_store(a1, dst + v + stride);
-    __builtin_nontemporal_store(a2, dst + v + 2 * stride);
-    __builtin_nontemporal_store(a3, dst + v + 3 * stride);
+                                                  int nslots, int E, int64_t nvec) {
+  __shared__ int s_slot[kPfWin], s_exp[kPfWin];
+  __shared__ int s_w[4];
+  const int tid = threadIdx.x, wv = tid / kWave;
+  for (int base = 0; base < nslots; base += kPfWin) {
+    __syncthreads();                                          // last window's list is done
+    int cnt = 0;
+    for (int r0 = 0; r0 < kPfWin && base + r0 < nslots; r0 += 256) {
+      const int i = base + r0 + tid;
+      const int e = i < nslots ? slot_expert[i] : -1;
+      const bool ok = e >= 0 && e < E;
+      const uint64_t m = __ballot(ok);
+      if (lane_id() == 0) s_w[wv] = __popcll(m);
+      __syncthreads();
+      int off = cnt, tot = 0;
+      for (int x = 0; x < 4; ++x) {
+        const int c = s_w[x];
+        if (x < wv) off += c;
+        tot += c;
+      }
+      if (ok) {
+        const int p = off + __popcll(m & lanemask_lt());
+        s_slot[p] = i;
+        s_exp[p] = e;
+      }
+      cnt += tot;
+      __syncthreads();                                        // s_w is reused
+    }
+    if (cnt == 0) continue;
+    const int CH = max(64, ((int)gridDim.x + cnt - 1) / cnt);
+    const int64_t stride = int64_t(CH) * 256;
+    for (int vb = blockIdx.x; vb < cnt * CH; vb += gridDim.x) {
+      const int j = vb / CH, c = vb - j * CH;
+      const u32x4* src = w_home + int64_t(s_exp[j]) * nvec;
+      u32x4* dst = w_pref + int64_t(s_slot[j]) * nvec;
+      int64_t v = int64_t(c) * 256 + tid;
+      constexpr int U = 4;       // loads in flight per thread (8 and 12 measured the same)
+      for (; v + (U - 1) * stride < nvec; v += U * stride) {
+        u32x4 a[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) a[q] = src[v + q * stride];
+#pragma unroll
+        for (int q = 0; q < U; ++q) __builtin_nontemporal_store(a[q], dst + v + q * stride);
+      }
+      for (; v < nvec; v += stride) __builtin_nontemporal_store(src[v], dst + v);
+    }
   }
-  for (; v < nvec; v += stride) __builtin_nontemporal_store(src[v], dst + v);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,11 +427,12 @@ extern "C" int moe_prefetch_weight(const moe_cfg* cfg, const moe_plan* plan,
   if (!w_home || !w_pref) return MOE_EINVAL;
   if (!aligned16(w_home, w_pref)) return MOE_EINVAL;
   const int64_t nvec = int64_t(cfg->H) * cfg->Hp / 8;
-  int chunks = (int)std::min<int64_t>(64, (nvec + 256 * 16 - 1) / (256 * 16));
-  if (chunks < 1) chunks = 1;
-  hipLaunchKernelGGL(k_prefetch, dim3(chunks, (unsigned)RB), dim3(256), 0, stream,
+  // enough workgroups to fill the chip (8 per CU); the grid depends on the
+  // shape only, never on how many slots the plan uses
+  const int grid = (int)std::min<int64_t>(2048, RB * 64);
+  hipLaunchKernelGGL(k_prefetch, dim3(grid), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(w_home), reinterpret_cast<u32x4*>(w_pref),
-                     plan->slot_expert, nvec);
+                     plan->slot_expert, (int)RB, cfg->E, nvec);
   return hip_status();
 }
 

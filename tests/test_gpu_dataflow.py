@@ -232,3 +232,40 @@ def test_wgrad_rejects_inference_mode():
                                   torch.zeros(mx.moe_gemm_workspace_size(c), dtype=torch.uint8,
                                               device="cuda"))
     del t
+
+
+@pytest.mark.parametrize("R,E,S,K,H,Hp,kind", [
+    (64, 2048, 64, 8, 16, 8, "theorem2_rev"),  # 2048 slot entries: the receivers' slots
+                                               # lie in the second compaction window
+    (128, 2048, 32, 8, 72, 40, "theorem2"),   # a row of 360 vectors (not a multiple of 256)
+    (32, 1024, 128, 8, 64, 24, "zipf"),
+    (8, 64, 64, 4, 8, 8, "hot"),              # one vector per thread at most
+])
+def test_prefetch_many_slots(R, E, S, K, H, Hp, kind):
+    """Every used slot bit-exact and every unused slot untouched, whether a
+    few or most slots hold an expert and across several windows of slot
+    entries."""
+    shape = W.TINY.with_(name="pf", R=R, E=E, S=S, K=K, H=H, Hp=Hp, B=E // R)
+    announce("prefetch many slots", shape, kind)
+    c, oc = cfgs(shape)
+    if kind == "theorem2_rev":
+        # Theorem-2 routing with expert ids mirrored: the last rank's experts
+        # get no tokens, so the last ranks receive
+        ids = shape.E - 1 - W.routing_theorem2(shape)
+    else:
+        ids, _ = routing(shape, kind, 10.0 if kind == "zipf" else 0)
+    ref = make_plan(ids, oc)
+    plan, g = gpu_plan(shape, ids)
+    assert_plan_equal(g, ref, shape)
+    w_home = W.randn_bf16((shape.E, shape.H, shape.Hp), 91, "cuda")
+    w_pref = torch.full((shape.R * shape.B, shape.H, shape.Hp), SENT, dtype=torch.int16,
+                        device="cuda").view(torch.bfloat16)
+    mx.moe_prefetch_weight(c, plan, w_home, w_pref)
+    torch.cuda.synchronize()
+    ref_pref = dataflow.prefetch(bits(w_home), ref, oc).reshape(shape.R * shape.B, H, Hp)
+    used = ref.slot_expert.reshape(-1) >= 0
+    gp = bits(w_pref)
+    announce("slots used", int(used.sum()), "of", used.size)
+    assert used.sum() > 0
+    assert np.array_equal(gp[used], ref_pref[used])
+    assert np.all(gp[~used] == SENT)
