@@ -706,6 +706,43 @@ def _time_calls(f, reps):
     return float(np.median(ts))
 
 
+def measure_vendor(path, reps):
+    """Context for the GEMM's roofline fraction: the same product shape as one
+    rank's work (65,536 rows x H=7168 -> H'=2048, 1.924 TFLOP) as (a) this
+    library's kernel on a single segment (a one-rank, one-expert layout),
+    (b) hipBLASLt through torch.matmul on the same operands (a comparator
+    only; nothing on the path calls it), and (c) this library's grouped GEMM
+    on rank 0 of the step's plan (ragged segments)."""
+    s, dev = path.shape, "cuda"
+    rows = s.SK
+    flops = 2.0 * rows * s.H * s.Hp
+    c1 = mx.make_cfg(1, rows, 1, 1, s.H, s.Hp, 0, mx.MODE_INFER)
+    cu1 = torch.tensor([0, rows], dtype=torch.int32, device=dev)
+    ws1 = torch.empty(mx.moe_gemm_workspace_size(c1), dtype=torch.uint8, device=dev)
+    xp = path.xperm[:rows]
+    w0 = path.w_home[0]
+    y1 = torch.empty((rows, s.Hp), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty_like(y1)
+    ours = _time_calls(lambda: mx.moe_grouped_gemm(c1, xp, path.w_home[:1], None, cu1, y1, 0, 1,
+                                                   ws1), reps)
+    vendor = _time_calls(lambda: torch.matmul(xp, w0, out=y2), reps)
+    grouped = _time_calls(lambda: mx.moe_grouped_gemm(path.c, path.xperm, path.w_home,
+                                                      path.w_pref, path.plan.cu_seqlens, path.y,
+                                                      0, 1, path.ws), reps)
+    torch.cuda.synchronize()
+    same = bool(torch.allclose(y1.float()[:4096], y2.float()[:4096], rtol=2e-2, atol=2e-2))
+    out = {"workload": "one rank's product shape: [65536, 7168] x [7168, 2048] bf16, fp32 "
+                       "accumulation, bf16 output (1.924 TFLOP); median of %d calls" % reps,
+           "this_library_one_segment": {"ms": ours, "TFLOPs": flops / ours / 1e9},
+           "hipblaslt_torch_matmul": {"ms": vendor, "TFLOPs": flops / vendor / 1e9,
+                                      "note": "comparator only, not on the path"},
+           "this_library_rank0_grouped": {"ms": grouped, "TFLOPs": flops / grouped / 1e9,
+                                          "note": "rank 0 of the step's plan, ragged segments"},
+           "outputs_agree_first_4096_rows": same}
+    del y1, y2, ws1
+    return out
+
+
 def measure_graph(path, reps):
     """The step captured once as a HIP graph (static shapes, no host sync in
     any call) and replayed, against the same calls issued eagerly: at the
@@ -932,8 +969,9 @@ def main():
                     "at every maxvio of the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the SwiGLU-expert and prefetch-pool blocks (they launch k_gemm<0>, "
-                         "k_prefetch and k_reduce_grad at other shapes; profiles of the step "
+                    help="skip the blocks after the step's own (small shapes, graph replay, "
+                         "Theorem-2, SwiGLU expert, prefetch pool, vendor GEMM context, Large-E: "
+                         "they launch the step's kernels at other shapes; profiles of the step "
                          "use this)")
     ap.add_argument("--swiglu-only", action="store_true",
                     help="plan and dispatch once, then only the SwiGLU-expert block")
@@ -1088,6 +1126,8 @@ def main():
     log("dedup dispatch")
     line["dedup_dispatch"] = measure_dedup(path, max(3, args.steps // 2))
     if not args.no_extras:
+        log("vendor GEMM context (one rank's product shape)")
+        line["vendor_gemm_context"] = measure_vendor(path, 5)
         log("tiny and skewed shapes")
         line["small_shapes"] = measure_small(10)
         log("graph capture and replay")

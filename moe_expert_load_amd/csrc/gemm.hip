@@ -64,6 +64,13 @@ constexpr int BM = 256, BN = 256;
 #endif
 constexpr int kGemmThreads = 256;
 
+// Row tiles per band of the column-tile-major work order (a segment of at
+// most this many row tiles is one band).
+#ifndef MOONEP_GEMM_BAND
+#define MOONEP_GEMM_BAND 8
+#endif
+constexpr int kBand = MOONEP_GEMM_BAND;
+
 enum { MODE_FWD = 0, MODE_WGRAD = 1, MODE_DGRAD = 2, MODE_SWIGLU = 3 };
 
 struct WorkItem {
@@ -341,15 +348,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     int tm, tn;
     WorkItem it;
     if (kNMajor) {
-      // Column-tile major inside a segment: the segment of row tiles
-      // [first, first + cnt) owns work [first*ntn, (first + cnt)*ntn), and
-      // w there is (tn, row tile) = divmod(w - first*ntn, cnt).  Neighbouring
-      // work shares one weight panel across the segment's row tiles.
+      // Column-tile major inside bands of kBand row tiles of a segment: the
+      // segment of row tiles [first, first + cnt) owns work
+      // [first*ntn, (first + cnt)*ntn); band b holds its row tiles
+      // [b*kBand, b*kBand + bc) and, inside the band, w is
+      // (tn, row tile) = divmod(w - band start, bc).  Neighbouring work shares
+      // one weight panel across the band's row tiles, and a long segment's
+      // rows are streamed once per band instead of once per column tile.
       const WorkItem h = item_at(w / ntn);
       const int loc = (int)(w - int64_t(h.first) * ntn);
+      const int b = loc / (kBand * ntn);
+      const int bc = min(kBand, h.cnt - b * kBand);
+      const int l = loc - b * kBand * ntn;
       tm = 0;
-      tn = loc / h.cnt;
-      it = item_at(h.first + loc % h.cnt);
+      tn = l / bc;
+      it = item_at(h.first + b * kBand + l % bc);
     } else {
       const int64_t item = w / (ntm * ntn);
       const int rest = (int)(w % (ntm * ntn));
