@@ -584,6 +584,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       mfma16(fa0, fb0);
       read_frags(S_, 1, fa1, fb1);
       interleave();
+      // Second half of the previous stage's refill (k-tile kt + kNST - 1;
+      // its first half went out in the previous step's last substep), so a
+      // stage's loads are spread over two substeps of MFMAs instead of one.
+      // Loads keep their issue order, so publish's in-flight counts hold.
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt > 0 && kt + kNST - 1 < nk)
+        issue_part(std::integral_constant<int, (S + kNST - 1) % kNST>(), kt + kNST - 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (SUB == 4) {
         mfma16(fa1, fb1);
         read_frags(S_, 2, fa0, fb0);
@@ -596,8 +604,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // Last substep: its fragments are in registers, so its 16 MFMAs cover
       // the hand-over -- publish k-tile kt+1 (all waves are done with stage
       // S past that barrier), read substep 0 of the next stage (stale and
-      // unused after the last k-tile) and refill stage S with k-tile
-      // kt + kNST -- instead of the matrix pipe idling through it.
+      // unused after the last k-tile) and start refilling stage S with
+      // k-tile kt + kNST (the other half follows in the next step's first
+      // substep) -- instead of the matrix pipe idling through it.
       mfma_row(fa1, fb1, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (kt + 1 < nk) publish(kt + 1);
@@ -608,8 +617,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       if (kt + kNST < nk) issue_part(std::integral_constant<int, S>(), kt + kNST, 0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_row(fa1, fb1, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + kNST < nk) issue_part(std::integral_constant<int, S>(), kt + kNST, 1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_row(fa1, fb1, 3);
       __builtin_amdgcn_sched_barrier(0);
