@@ -269,3 +269,39 @@ def test_prefetch_many_slots(R, E, S, K, H, Hp, kind):
     assert used.sum() > 0
     assert np.array_equal(gp[used], ref_pref[used])
     assert np.all(gp[~used] == SENT)
+
+
+@pytest.mark.parametrize("H,Hp", [(72, 520), (600, 72)])
+def test_long_segments_band_order(H, Hp):
+    """Segments of 2,600 rows (10 full row tiles and a ragged one: one band of
+    8 row tiles and a second band of 3) over several column tiles: the
+    forward GEMM (3 column tiles when H'=520) and the data-gradient GEMM (3
+    column tiles when H=600), every output row against the oracle, with a
+    home segment on rank 0 and a prefetch-slot segment on rank 1."""
+    shape = W.TINY.with_(name="band", R=2, E=2, S=2600, K=1, B=1, H=H, Hp=Hp)
+    announce("long segments", shape)
+    c, oc = cfgs(shape)
+    ids = W.routing_hot(shape)
+    ref = make_plan(ids, oc)
+    plan, g = gpu_plan(shape, ids)
+    assert_plan_equal(g, ref, shape)
+    assert (np.diff(ref.cu_seqlens, axis=1).max(axis=1) > 8 * 256).all()
+    x = W.randn_bf16((shape.tokens, H), 41, "cuda")
+    w_home = W.randn_bf16((shape.E, H, Hp), 42, "cuda")
+    dy = W.randn_bf16((shape.R * shape.SK, Hp), 43, "cuda")
+    w_pref = torch.empty((shape.R * shape.B, H, Hp), dtype=torch.bfloat16, device="cuda")
+    xperm = torch.empty((shape.R * shape.SK, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((shape.R * shape.SK, Hp), dtype=torch.bfloat16, device="cuda")
+    dxp = torch.empty((shape.R * shape.SK, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device="cuda")
+    mx.moe_prefetch_weight(c, plan, w_home, w_pref)
+    mx.moe_dispatch(c, plan, x, xperm)
+    mx.moe_grouped_gemm(c, xperm, w_home, w_pref, plan.cu_seqlens, y, 0, shape.R, ws)
+    mx.moe_grouped_gemm_dgrad(c, dy, w_home, w_pref, plan.cu_seqlens, dxp, 0, shape.R, ws)
+    torch.cuda.synchronize()
+    wb = bits(w_home)
+    ref_pref = dataflow.prefetch(wb, ref, oc)
+    ref_xp = dataflow.dispatch(bits(x), ref, oc)
+    assert np.array_equal(bits(xperm), ref_xp)
+    rows_close(bits(y), dataflow.grouped_gemm(ref_xp, wb, ref_pref, ref, oc))
+    rows_close(bits(dxp), dataflow.dgrad(bits(dy), wb, ref_pref, ref, oc))
