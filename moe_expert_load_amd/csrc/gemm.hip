@@ -476,6 +476,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) load_lds16(ra, Ap + (wv * 8 + u) * 1024, gop[u], ka);
     };
+    // Half h of those loads (pieces u in [4h, 4h + 4)).
+    auto issue_a_pair_half = [&](int p, int h) {
+      unsigned char* Ap = pair_buf(p);
+      const uint32_t ka = uint32_t(p) * 64 * 2;
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const int u = 4 * h + u2;
+        load_lds16(ra, Ap + (wv * 8 + u) * 1024, gop[u], ka);
+      }
+    };
     auto read_frags_pair = [&](auto S_, int kt, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
       constexpr int S = decltype(S_)::value;
       const unsigned char* Ap = pair_buf(kt >> 1) + rp_off[kt & 1][s];
@@ -624,7 +634,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 
     // Paired mode.  Issue order (per wave): A0, B0, B1, A1, B2, B3, A2 before
     // the loop, then at step kt: B(kt+4), and for odd kt the pair
-    // (kt+1)/2 + 2 (into the buffer of the pair just finished).  Loads
+    // (kt+1)/2 + 2 (into the buffer of the pair just finished; its second
+    // half goes out in the next step's first substep, before that step's
+    // publish, so the counts below are unchanged).  Loads
     // complete in order, so at publish(kt+1) everything issued after B(kt+1)
     // may stay in flight: A(8) + B(4) + B(4) + A(8) = 24 loads for even kt,
     // B(4) + B(4) + A(8) = 16 for odd kt -- as long as all of them exist
@@ -667,6 +679,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       mfma16(fa0, fb0);
       read_frags_pair(S_, kt, 1, fa1, fb1);
       interleave();
+      // Second half of the A pair whose first half the previous (odd) step
+      // issued: same issue order, so publish_pair's in-flight counts hold.
+      __builtin_amdgcn_sched_barrier(0);
+      if (!(kt & 1) && kt > 0 && 2 * (kt / 2 + 2) < nk) issue_a_pair_half(kt / 2 + 2, 1);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
       mfma_row(fa1, fb1, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -679,7 +696,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       mfma_row(fa1, fb1, 2);
       __builtin_amdgcn_sched_barrier(0);
-      if ((kt & 1) && 2 * ((kt + 1) / 2 + 2) < nk) issue_a_pair((kt + 1) / 2 + 2);
+      if ((kt & 1) && 2 * ((kt + 1) / 2 + 2) < nk) issue_a_pair_half((kt + 1) / 2 + 2, 0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_row(fa1, fb1, 3);
       __builtin_amdgcn_sched_barrier(0);
