@@ -16,7 +16,10 @@ the same way and reported beside the step ("data_backward"), outside
 `value`, and so are the two-projection SwiGLU expert's kernels at the same
 shape ("swiglu_expert": first projection [E+B, 7168, 2*2048] fused with
 the activation, second projection [E+B, 2048, 7168], activation backward),
-a two-layer backward sharing one prefetch pool ("prefetch_pool"), the
+a two-layer backward sharing one prefetch pool ("prefetch_pool"), one
+rank's product shape as a single segment beside hipBLASLt through
+torch.matmul on the same operands (a comparator only,
+"vendor_gemm_context"), the
 Theorem-2 worst case at the same shape, training and inference B=4
 ("theorem2"), and the
 Large-E shape (R=64, S=4096, E=896, K=16): plan, dispatch and combine over
@@ -25,6 +28,7 @@ Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
                     [--sweep] [--no-cpu-baseline] [--no-extras] [--swiglu-only]
+                    [--vendor-only]
 """
 import argparse
 import json
@@ -101,6 +105,13 @@ def _short_kernel(name):
         # tuning variants of one kernel
         keep = m.group(1) in ("k_gemm", "k_sched")
         return m.group(1) + ((m.group(2) or "") if keep else "")
+    if name.startswith("Cijk_"):
+        # the vendor library's GEMM (comparator only): keep its macro tile
+        # and matrix instruction from the kernel name
+        t = re.search(r"_MT(\w+?)_", name)
+        mi = re.search(r"_MI(\w+?)_", name)
+        return "hipBLASLt %s MT%s MI%s" % (name.split("_")[0], t.group(1) if t else "?",
+                                            mi.group(1) if mi else "?")
     return "copyBuffer" if "copyBuffer" in name else None
 
 
@@ -973,6 +984,8 @@ def main():
                          "Theorem-2, SwiGLU expert, prefetch pool, vendor GEMM context, Large-E: "
                          "they launch the step's kernels at other shapes; profiles of the step "
                          "use this)")
+    ap.add_argument("--vendor-only", action="store_true",
+                    help="plan and dispatch once, then only the vendor GEMM context block")
     ap.add_argument("--swiglu-only", action="store_true",
                     help="plan and dispatch once, then only the SwiGLU-expert block")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -1015,6 +1028,11 @@ def main():
     log("allocating and generating inputs")
     path = Path(shape, ids, gates)
     torch.cuda.synchronize()
+    if args.vendor_only:
+        path.run(1, timed=False, only=("plan", "prefetch", "dispatch"))
+        torch.cuda.synchronize()
+        print(json.dumps({"vendor_gemm_context": measure_vendor(path, 8)}), flush=True)
+        return
     if args.swiglu_only:
         path.run(1, timed=False, only=("plan", "dispatch"))
         torch.cuda.synchronize()
