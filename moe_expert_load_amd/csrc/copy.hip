@@ -103,7 +103,10 @@ __global__ __launch_bounds__(256) void k_dispatch(const u32x4* __restrict__ x,
       const int c = c0 + u * kWave + lane;
       if (c < hv) v[u] = src[c];
     }
-    for (int k = 0; k < K; ++k) {
+    // Each token starts at its own k (t mod K), so the tokens in flight do
+    // not all write their top-1 copy (the hot experts' segments) at once.
+    for (int kk = 0; kk < K; ++kk) {
+      const int k = (kk + t) % K;
       const int dst = __shfl(myroute, k, kWave);
       if (dst < 0) continue;
       u32x4* d = xperm + int64_t(dst) * hv;
