@@ -76,11 +76,20 @@ KERNEL_SOURCES = {"k_gemm<0>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_route": "moe_expert_load_amd/csrc/plan.hip"}
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed, so an edit
+    to comments alone does not void the counters taken for the code."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel):
     import hashlib
     h = hashlib.sha256()
     for rel in (KERNEL_SOURCES[kernel], "moe_expert_load_amd/csrc/common.hpp"):
-        h.update(open(os.path.join(ROOT, rel), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, rel), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

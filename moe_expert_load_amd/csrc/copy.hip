@@ -1,7 +1,8 @@
 // HBM-bound steps: prefetch_weight, fused permute (dispatch), gate-weighted
-// combine and reduce_grad, and the backward of combine and of dispatch.  Every row moves as 16-byte vectors; a wave owns a
-// token (dispatch, combine) so its K routes are read once and broadcast with
-// lane shuffles.
+// combine and reduce_grad, and the backward of combine and of dispatch.
+// Every row moves as 16-byte vectors; a workgroup (dispatch) or a wave
+// (combine and the backward kernels) owns a token, so its K routes are read
+// once and broadcast with lane shuffles.
 //
 // Sources: "Kimi K3 模型结构（8）：训练并行，MoonEP 与四类等待", heading
 // 在线规划、零拷贝、静态 shape (permute straight into expert-grouped places;

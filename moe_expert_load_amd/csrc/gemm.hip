@@ -15,10 +15,11 @@
 //   k_gemm<MODE> a persistent grid, one 256-thread workgroup per CU, pulls
 //               256x256 output tiles from that list.  Consecutive work items
 //               go to the 32 workgroups of one XCD (blockIdx % 8 picks the
-//               XCD); inside a segment of row tiles the forward and the data
-//               gradient go column tile by column tile, so the CUs of one
-//               XCD share each weight panel across all of the segment's row
-//               tiles in that XCD's L2.
+//               XCD); inside bands of 8 row tiles of a segment the forward
+//               and the data gradient go column tile by column tile, so the
+//               CUs of one XCD share each weight panel across the band's row
+//               tiles in that XCD's L2, and a long segment streams its rows
+//               once per band rather than once per column tile.
 //   MODE 0: y = xperm_seg @ W (forward); MODE 1: G = xperm_seg^T @ dy_seg
 //   (weight gradient, fp32); MODE 2: dxperm_seg = dy_seg @ W^T (data
 //   gradient, over the forward's work list); MODE 3: the first projection

@@ -29,3 +29,33 @@ def test_stats_summary_from_a_small_csv(tmp_path):
     text = out.read_text()
     assert "| k_gemm<1> | 2 | 17000.0 |" in text
     assert "| k_dispatch | 2 | 1600.0 |" in text
+
+
+def test_source_digest_ignores_comments_only():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = "int f(int x) {  // one\n  return x + 1; /* two\n lines */ }\n"
+    b = "int f(int x) {\n  return x + 1; }  // changed comment\n"
+    c = "int f(int x) {\n  return x + 2; }\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_committed_traffic_matches_the_current_kernels():
+    """The HBM-traffic summary under profiles/ was taken for the current code
+    of every kernel of the step (re-take it with the commands it names after
+    changing a kernel); otherwise the bench reports traffic as null."""
+    sys.path.insert(0, ROOT)
+    import bench
+    stale = [k for k in ("k_gemm<0>", "k_gemm<1>", "k_dispatch", "k_combine", "k_prefetch",
+                         "k_reduce_grad") if bench.measured_traffic(k) is None]
+    assert not stale, "traffic summary predates the code of %s" % stale
+
+
+def test_vendor_kernel_rows_are_named_by_tile():
+    sys.path.insert(0, ROOT)
+    import bench
+    name = "Cijk_Ailk_Bljk_BBS_BH_Bias_HA_S_SAV_UserArgs_MT256x256x64_MI16x16x1_SN_LDSB1"
+    assert bench._short_kernel(name) == "hipBLASLt Cijk MT256x256x64 MI16x16x1"
+    assert bench._short_kernel("void moonep::k_gemm<2>(moonep::GemmArgs)") == "k_gemm<2>"
+    assert bench._short_kernel("void moonep::k_route<true>(moonep::PlanArgs)") == "k_route"
