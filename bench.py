@@ -726,6 +726,29 @@ def _time_calls(f, reps):
     return float(np.median(ts))
 
 
+def measure_ceilings(reps=5, gib=4):
+    """Context for the HBM fractions: what plain device kernels reach on this
+    card (torch's own copy, fill and sum over 4 GiB; not the path): a copy
+    reads and writes every byte, a fill only writes, a sum only reads."""
+    n = gib << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    av = a.view(torch.float32)
+    out = {"workload": "%d GiB buffers; median of %d calls" % (gib, reps)}
+    t = _time_calls(lambda: b.copy_(a), reps)
+    out["copy_GBps"] = 2.0 * n / t / 1e6
+    t = _time_calls(lambda: b.fill_(3), reps)
+    out["fill_GBps"] = 1.0 * n / t / 1e6
+    t = _time_calls(lambda: av.sum(), reps)
+    out["read_GBps"] = 1.0 * n / t / 1e6
+    out["note"] = ("torch device kernels on this card, for context; nothing on the path uses "
+                   "them; read_GBps is torch's sum, a reduction kernel rather than a pure read")
+    del a, b, av
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_vendor(path, reps):
     """Context for the GEMM's roofline fraction: the same product shape as one
     rank's work (65,536 rows x H=7168 -> H'=2048, 1.924 TFLOP) as (a) this
@@ -1116,6 +1139,8 @@ def main():
         "roofline": roofline,
         "rooflines": roof,
     }
+    log("HBM ceilings of plain device kernels (context)")
+    line["hbm_ceilings"] = measure_ceilings()
     log("planner policies at the bench shape")
     pol = {}
     for t in W.MAXVIO_SWEEP["bench"]:
