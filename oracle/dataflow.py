@@ -9,14 +9,19 @@ tolerances in the parity tests cover.
 
 Pinned by tests/test_oracle_dataflow.py: bit-copy invariants of permute and
 prefetch, closed forms with W[e] = c_e * I and constant gates, brute-force
-triple loops on tiny shapes, known constants for reduce_grad, and for the
-backward maps the adjoint identities <dout, F(x)> = <F^T(dout), x> with
-small-integer data (exact in bf16 and float64).
+triple loops on tiny shapes, known constants for reduce_grad (and hand sums
+for its tolerance scale ``reduce_terms_abs``), and for the backward maps the
+adjoint identities <dout, F(x)> = <F^T(dout), x> with small-integer data
+(exact in bf16 and float64).  The sampled forms used at full sizes
+(``dispatch_rows``, ``gemm_rows``, ``combine_tokens``, ``wgrad_entries``,
+``combine_backward_tokens``, ``dgrad_rows``, ``dispatch_backward_tokens``,
+``route_encode_tokens``) are each pinned to their full form on small
+shapes; every step is also pinned on a failed plan (no routes, no
+segments), where it reduces to writing nothing or to empty sums.
 """
 import numpy as np
 
 from . import bf16
-from .plan import segment_of_rows
 
 
 def dispatch(x_bits, plan, cfg):
@@ -25,14 +30,39 @@ def dispatch(x_bits, plan, cfg):
     [K3-blog] "在线规划、零拷贝、静态 shape" / [MoonEP-fr] "Communication sans
     copie": the plan gives each routing entry its place in the destination
     rank's expert-grouped S*K buffer and the row is written there directly.
-    Returns the [R*S*K, H] bit array (R stacked [S*K, H] buffers).
+    Returns the [R*S*K, H] bit array (R stacked [S*K, H] buffers).  A slot
+    whose route is -1 (no plan) has no place and writes nothing; rows that
+    no route names stay zero.
     """
     K = cfg.K
     x = np.asarray(x_bits, np.uint16)
     out = np.zeros((cfg.R * cfg.SK, cfg.H), np.uint16)
-    src_tok = np.arange(plan.route.size) // K
-    out[plan.route] = x[src_tok]
+    ok = plan.route >= 0
+    src_tok = np.arange(plan.route.size)[ok] // K
+    out[plan.route[ok]] = x[src_tok]
     return out
+
+
+def _route_inverse(plan):
+    """inv[q] = the slot whose route is row q, or -1 if no route names q."""
+    inv = np.full(plan.route.size, -1, np.int64)
+    ok = plan.route >= 0
+    inv[plan.route[ok]] = np.nonzero(ok)[0]
+    return inv
+
+
+def dispatch_rows(rows, x_bits, plan, cfg):
+    """``dispatch`` for selected destination rows only (large shapes).
+
+    Row q holds token inv(q) // K, where inv(q) is the slot routed to q.
+    ``x_bits`` may be any object whose ``[index array]`` gives bf16 rows.
+    Every listed row must be named by some route.
+    """
+    rows = np.asarray(rows, np.int64)
+    slot = _route_inverse(plan)[rows]
+    if np.any(slot < 0):
+        raise ValueError("a listed row is not the destination of any slot")
+    return np.asarray(x_bits[slot // cfg.K], np.uint16)
 
 
 def prefetch(w_home_bits, plan, cfg):
@@ -93,8 +123,7 @@ def gemm_rows(rows, x_bits, w_home_bits, w_pref_bits, plan, cfg):
     """
     SK = cfg.SK
     rows = np.asarray(rows, np.int64)
-    inv = np.empty(plan.route.size, np.int64)
-    inv[plan.route] = np.arange(plan.route.size)
+    inv = _route_inverse(plan)
     seg = np.empty(rows.size, np.int64)
     for idx, q in enumerate(rows):
         r, off = divmod(int(q), SK)
@@ -116,7 +145,8 @@ def combine(y_bits, gates, plan, cfg):
 
     [K3-blog] "在线规划、零拷贝、静态 shape": each expert output is multiplied
     by its own fp32 router weight on combine; [TSR] §6.1: combine then
-    weighted sum.  Accumulated in float64, rounded to bf16 once.
+    weighted sum.  Accumulated in float64, rounded to bf16 once.  A route of
+    -1 (no plan) contributes nothing, so a token without any route gets 0.
     """
     K = cfg.K
     g = np.asarray(gates, np.float64).reshape(-1, K)
@@ -125,7 +155,27 @@ def combine(y_bits, gates, plan, cfg):
     route = plan.route.reshape(nt, K)
     y = np.asarray(y_bits, np.uint16)
     for k in range(K):
-        acc += g[:, k:k + 1] * bf16.bits_to_f64(y[route[:, k]])
+        ok = route[:, k] >= 0
+        acc[ok] += g[ok, k:k + 1] * bf16.bits_to_f64(y[route[ok, k]])
+    return bf16.f64_to_bits(acc)
+
+
+def combine_tokens(toks, y_bits, gates, plan, cfg):
+    """``combine`` for selected tokens only (large shapes).
+
+    ``y_bits`` may be any object whose ``[index array]`` gives bf16 rows;
+    only the K rows each listed token routes to are read.  Same definition
+    and order: k ascending, float64, one rounding, routes of -1 skipped.
+    """
+    K = cfg.K
+    toks = np.asarray(toks, np.int64)
+    g = np.asarray(gates, np.float64).reshape(-1, K)[toks]
+    route = plan.route.reshape(-1, K)[toks]
+    acc = np.zeros((toks.size, cfg.Hp), np.float64)
+    for k in range(K):
+        ok = route[:, k] >= 0
+        if ok.any():
+            acc[ok] += g[ok, k:k + 1] * bf16.bits_to_f64(np.asarray(y_bits[route[ok, k]]))
     return bf16.f64_to_bits(acc)
 
 
@@ -157,6 +207,28 @@ def wgrad(xperm_bits, dy_bits, plan, cfg):
     return gh, gp
 
 
+def wgrad_entries(r, j, hs, x_bits, dy_bits, plan, cfg):
+    """Rows ``hs`` of the weight gradient G(r, j) = xperm_seg^T @ dy_seg.
+
+    For large shapes: the segment's permuted rows are taken from the tokens
+    through the dispatch definition (row q holds x[inv(q) // K]), so only
+    the columns ``hs`` of those token rows and the segment's dy rows are
+    read.  ``x_bits`` / ``dy_bits`` may be any object whose ``[index array]``
+    gives bf16 rows.  float64; returns [len(hs), H'].  An empty segment
+    gives zeros (what the home rows get, see ``wgrad``).
+    """
+    SK = cfg.SK
+    hs = np.asarray(hs, np.int64)
+    lo, hi = int(plan.cu_seqlens[r, j]), int(plan.cu_seqlens[r, j + 1])
+    if hi == lo:
+        return np.zeros((hs.size, cfg.Hp), np.float64)
+    rows = np.arange(r * SK + lo, r * SK + hi)
+    toks = _route_inverse(plan)[rows] // cfg.K
+    xs = bf16.bits_to_f64(np.asarray(x_bits[toks])[:, hs])        # [len, |hs|]
+    ds = bf16.bits_to_f64(np.asarray(dy_bits[rows]))              # [len, H']
+    return xs.T @ ds
+
+
 def reduce_grad(grad_home, grad_pref, plan, cfg):
     """reduce_grad: fold prefetch-slot gradients into their home rows.
 
@@ -180,7 +252,11 @@ def reduce_grad(grad_home, grad_pref, plan, cfg):
 
 
 def reduce_terms_abs(grad_home, grad_pref, plan, cfg):
-    """sum of |terms| per element of each home row's reduction (tolerances)."""
+    """Per element of grad_home, the sum of the magnitudes of the terms that
+    ``reduce_grad`` adds there: |grad_home[e]| plus |grad_pref[r, b]| over
+    every slot with slot_expert[r, b] = e.  It scales the fp32 tolerance of
+    the reduction (the sum's rounding error is bounded by a multiple of it).
+    """
     s = np.abs(np.asarray(grad_home, np.float64)).copy()
     for r in range(cfg.R):
         for b in range(cfg.B):
@@ -190,9 +266,6 @@ def reduce_terms_abs(grad_home, grad_pref, plan, cfg):
     return s
 
 
-__all__ = ["dispatch", "prefetch", "weight_row", "grouped_gemm", "gemm_rows",
-           "combine", "wgrad", "reduce_grad", "reduce_terms_abs",
-           "segment_of_rows"]
 
 
 def combine_backward(dout_bits, y_bits, gates, plan, cfg):
@@ -221,6 +294,33 @@ def combine_backward(dout_bits, y_bits, gates, plan, cfg):
         dy[q] = bf16.f64_to_bits(g[ok, k:k + 1] * d[ok])
         dg[ok, k] = np.sum(d[ok] * bf16.bits_to_f64(y[q]), axis=1)
     return dy, dg
+
+
+def combine_backward_tokens(toks, dout_bits, y_bits, gates, plan, cfg):
+    """``combine_backward`` for selected tokens only (large shapes).
+
+    For each listed token t and each k (ascending) with a route q >= 0:
+    dy[q] = bf16(g[t, k] * dout[t]) (the exact product rounded once) and
+    dgates[t, k] = sum_h dout[t, h] * y[q, h] (float64).  ``dout_bits`` and
+    ``y_bits`` may be any object whose ``[index array]`` gives bf16 rows.
+    Returns (rows [len(toks), K] -- the destination row of each (t, k), -1
+    for none --, dy bits [len(toks), K, H'] with zero rows where there is no
+    route, dgates [len(toks), K] with 0 there).
+    """
+    K = cfg.K
+    toks = np.asarray(toks, np.int64)
+    g = np.asarray(gates, np.float64).reshape(-1, K)[toks]
+    route = plan.route.reshape(-1, K)[toks].astype(np.int64)
+    d = bf16.bits_to_f64(np.asarray(dout_bits[toks]))
+    dy = np.zeros((toks.size, K, cfg.Hp), np.uint16)
+    dg = np.zeros((toks.size, K), np.float64)
+    for k in range(K):
+        ok = route[:, k] >= 0
+        if not ok.any():
+            continue
+        dy[ok, k] = bf16.f64_to_bits(g[ok, k:k + 1] * d[ok])
+        dg[ok, k] = np.sum(d[ok] * bf16.bits_to_f64(np.asarray(y_bits[route[ok, k]])), axis=1)
+    return route, dy, dg
 
 
 def dgrad(dy_bits, w_home_bits, w_pref_bits, plan, cfg, ranks=None):
@@ -282,6 +382,22 @@ def dispatch_backward(dxperm_bits, plan, cfg):
     return bf16.f64_to_bits(acc)
 
 
+def dispatch_backward_tokens(toks, dxperm_bits, plan, cfg):
+    """``dispatch_backward`` for selected tokens only (large shapes): the sum,
+    k ascending in float64, of the rows each listed token was copied to,
+    rounded once.  ``dxperm_bits`` may be any object whose ``[index array]``
+    gives bf16 rows; routes of -1 contribute nothing."""
+    K = cfg.K
+    toks = np.asarray(toks, np.int64)
+    route = plan.route.reshape(-1, K)[toks]
+    acc = np.zeros((toks.size, cfg.H), np.float64)
+    for k in range(K):
+        ok = route[:, k] >= 0
+        if ok.any():
+            acc[ok] += bf16.bits_to_f64(np.asarray(dxperm_bits[route[ok, k]]))
+    return bf16.f64_to_bits(acc)
+
+
 NO_DEST = -(2 ** 31)        # encoded route of a slot that has no destination
 
 
@@ -310,6 +426,26 @@ def route_encode(plan, cfg):
             enc[t, k] = q if d not in seen else -q - 1
             seen.add(d)
     return enc.reshape(-1).astype(np.int32)
+
+
+def route_encode_tokens(toks, plan, cfg):
+    """``route_encode`` for selected tokens only (large shapes): the same rule,
+    token by token, on the plan's routes.  Returns [len(toks), K] int64."""
+    K, SK = cfg.K, cfg.SK
+    toks = np.asarray(toks, np.int64)
+    route = plan.route.reshape(-1, K)[toks].astype(np.int64)
+    enc = np.empty_like(route)
+    for i in range(toks.size):
+        seen = set()
+        for k in range(K):
+            q = int(route[i, k])
+            if q < 0:
+                enc[i, k] = NO_DEST
+                continue
+            d = q // SK
+            enc[i, k] = q if d not in seen else -q - 1
+            seen.add(d)
+    return enc
 
 
 def dispatch_dedup(x_bits, enc, cfg):

@@ -256,10 +256,32 @@ def make_plan(topk_ids, cfg, policy=POLICY_ASCENDING):
                 route=route, status=status)
 
 
-def segment_of_rows(plan, cfg):
-    """For every destination row r*S*K + q: its weight row j (segment id)."""
-    R, E, B, SK = cfg.R, cfg.E, cfg.B, cfg.SK
-    seg = np.empty(R * SK, np.int64)
-    for r in range(R):
-        seg[r * SK:(r + 1) * SK] = np.repeat(np.arange(E + B), plan.seg_len[r])
-    return seg
+def failed_plan(topk_ids, cfg):
+    """The plan state when the ids cannot be planned: no plan at all.
+
+    The pages define the planner for valid router output only; an id outside
+    [0, E) has no expert to go to.  Reading taken for the library's error
+    contract: the ids that name a real expert are still counted (T_e and the
+    home loads over them), but nothing is moved and no slot gets a place --
+    no fills, every rank's buffer empty (cu_seqlens all zero), no prefetch
+    slot in use, every route -1 -- and the status carries STATUS_BAD_ID and,
+    since the valid slots then fall short of R*S*K, STATUS_UNBALANCED.  Every
+    later step then has no routes and no segments to work on.
+    """
+    R, E, B = cfg.R, cfg.E, cfg.B
+    ids = np.asarray(topk_ids).reshape(-1).astype(np.int64)
+    if ids.size != R * cfg.S * cfg.K:
+        raise ValueError("topk_ids must hold R*S*K entries")
+    ok = (ids >= 0) & (ids < E)
+    if ok.all():
+        raise ValueError("every id is valid: use make_plan")
+    T = histogram(ids[ok], E)
+    return Plan(counts=T, load0=home_loads(T, R),
+                rank_in_expert=np.full(ids.size, -1, np.int64),
+                moves=np.zeros((0, 4), np.int64), fills=[], taken=np.zeros(E, np.int64),
+                n_redundant=np.zeros(R, np.int64), src_rank=np.full(R, -1, np.int64),
+                slot_expert=np.full((R, B), -1, np.int64),
+                seg_len=np.zeros((R, E + B), np.int64),
+                cu_seqlens=np.zeros((R, E + B + 1), np.int64),
+                route=np.full(ids.size, -1, np.int64),
+                status=STATUS_BAD_ID | STATUS_UNBALANCED)

@@ -342,3 +342,170 @@ def test_route_encode_page_illustration():
     assert enc[0].tolist() == [0, -2, SK, 2 * SK, -(2 * SK + 1) - 1, -(SK + 1) - 1]
     assert enc[1].tolist() == [2, 3 * SK, -(3 * SK + 1) - 1, -(3 * SK + 2) - 1, -4, SK + 2]
     assert int((enc[0] >= 0).sum()) == 3
+
+
+# ---------------------------------------------------------------------------
+# The tolerance scale of reduce_grad, on a hand-built slot map with values
+# summed by hand (no call of the oracle's reduction).
+# ---------------------------------------------------------------------------
+class _SlotMap:
+    def __init__(self, slot_expert):
+        self.slot_expert = np.asarray(slot_expert, np.int64)
+
+
+def test_reduce_terms_abs_hand_values():
+    # R = 2 ranks, B = 2 slots, E = 4 experts; slot (1, 1) holds no expert.
+    cfg = Cfg(R=2, S=1, E=4, K=1, H=1, Hp=2, B=2)
+    plan = _SlotMap([[2, 3], [0, -1]])
+    gh = np.array([1.0, -2.0, 3.0, -4.0])[:, None, None] * np.ones((4, 1, 2))
+    gp = np.array([[-5.0, 6.0], [7.0, 8.0]])[:, :, None, None] * np.ones((2, 2, 1, 2))
+    gp[0, 0, 0, 1] = 0.25                           # one element differs
+    s = dataflow.reduce_terms_abs(gh, gp, plan, cfg)
+    # e=0: |1| + |7|; e=1: |-2| only; e=2: |3| + |-5| (second column |3|+0.25);
+    # e=3: |-4| + |6|; slot (1,1)'s 8 belongs to no expert
+    want = np.array([[8.0, 8.0], [2.0, 2.0], [8.0, 3.25], [10.0, 10.0]])[:, None, :]
+    assert np.array_equal(s, want)
+    # sums of magnitudes, not magnitudes of sums: opposite signs do not cancel
+    gh2 = np.full((4, 1, 2), -6.0)
+    s2 = dataflow.reduce_terms_abs(gh2, np.abs(gp), plan, cfg)
+    assert s2[2, 0, 0] == 11.0 and s2[1, 0, 0] == 6.0
+
+
+# ---------------------------------------------------------------------------
+# Sampled forms used at full sizes, each against its full form on small
+# shapes (train and inference plans, uniform, hot and Theorem-2 routing).
+# ---------------------------------------------------------------------------
+SAMPLED_CASES = [
+    (W.TINY, "uniform"), (W.TINY.with_(B=1, mode=1), "hot"),
+    (W.TINY.with_(R=2, E=8, K=3, S=10, B=4), "uniform"),
+    (W.ADVERSARIAL.with_(S=32, H=24, Hp=16), "theorem2"),
+]
+
+
+def _case(shape, kind, seed=0):
+    cfg = cfg_of(shape)
+    if kind == "hot":
+        ids, gates = W.routing_hot(shape), W.gates_uniform(shape)
+    elif kind == "theorem2":
+        ids, gates = W.routing_theorem2(shape), W.gates_uniform(shape)
+    else:
+        ids, gates = W.routing_uniform(shape, salt=seed)
+    return cfg, ids, gates, make_plan(ids, cfg)
+
+
+@pytest.mark.parametrize("shape,kind", SAMPLED_CASES)
+def test_sampled_forms_equal_full_forms(shape, kind):
+    g = np.random.default_rng(41)
+    cfg, ids, gates, plan = _case(shape, kind)
+    x = rand_bits(g, (shape.tokens, shape.H))
+    y = rand_bits(g, (shape.R * shape.SK, shape.Hp))
+    dout = rand_bits(g, (shape.tokens, shape.Hp))
+    dxp = rand_bits(g, (shape.R * shape.SK, shape.H))
+    dy_in = rand_bits(g, (shape.R * shape.SK, shape.Hp))
+    toks = np.unique(g.integers(0, shape.tokens, max(3, shape.tokens // 3)))
+    rows = np.unique(g.integers(0, shape.R * shape.SK, max(3, shape.R * shape.SK // 3)))
+    # dispatch
+    xp = dataflow.dispatch(x, plan, cfg)
+    assert np.array_equal(dataflow.dispatch_rows(rows, x, plan, cfg), xp[rows])
+    # combine
+    assert np.array_equal(dataflow.combine_tokens(toks, y, gates, plan, cfg),
+                          dataflow.combine(y, gates, plan, cfg)[toks])
+    # combine backward
+    dy_full, dg_full = dataflow.combine_backward(dout, y, gates, plan, cfg)
+    q, dy_s, dg_s = dataflow.combine_backward_tokens(toks, dout, y, gates, plan, cfg)
+    assert np.array_equal(q, plan.route.reshape(-1, shape.K)[toks])
+    for k in range(shape.K):
+        assert np.array_equal(dy_s[:, k], dy_full[q[:, k]])
+    assert np.array_equal(dg_s, dg_full[toks])
+    # dispatch backward
+    assert np.array_equal(dataflow.dispatch_backward_tokens(toks, dxp, plan, cfg),
+                          dataflow.dispatch_backward(dxp, plan, cfg)[toks])
+    # route encoding
+    assert np.array_equal(dataflow.route_encode_tokens(toks, plan, cfg),
+                          dataflow.route_encode(plan, cfg).reshape(-1, shape.K)[toks])
+    # weight gradient, train mode only
+    if cfg.mode == 0:
+        gh, gp = dataflow.wgrad(xp, dy_in, plan, cfg)
+        hs = np.unique(g.integers(0, shape.H, 5))
+        for r in range(shape.R):
+            for j in list(range(r * cfg.n, (r + 1) * cfg.n)) + list(range(cfg.E, cfg.E + cfg.B)):
+                got = dataflow.wgrad_entries(r, j, hs, x, dy_in, plan, cfg)
+                if j < cfg.E:
+                    want = gh[j][hs]
+                elif plan.slot_expert[r, j - cfg.E] >= 0:
+                    want = gp[r, j - cfg.E][hs]
+                else:
+                    assert not got.any()
+                    continue
+                assert np.allclose(got, want, rtol=1e-13, atol=1e-13), (r, j)
+
+
+def test_dispatch_rows_rejects_unnamed_rows():
+    shape = W.TINY
+    cfg, ids, _, plan = _case(shape, "uniform")
+    bad = _bad_ids(shape)
+    from oracle.plan import failed_plan
+    fp = failed_plan(bad, cfg)
+    x = np.zeros((shape.tokens, shape.H), np.uint16)
+    with pytest.raises(ValueError):
+        dataflow.dispatch_rows([0], x, fp, cfg)
+
+
+# ---------------------------------------------------------------------------
+# A failed plan (ids outside [0, E)): what every later step computes from its
+# definition when there is no route and no segment.
+# ---------------------------------------------------------------------------
+def _bad_ids(shape, salt=3):
+    ids, _ = W.routing_uniform(shape, salt=salt)
+    ids = ids.copy()
+    ids[1, 0] = shape.E + 2
+    ids[shape.tokens - 1, shape.K - 1] = -1
+    return ids
+
+
+@pytest.mark.parametrize("shape", [W.TINY, W.TINY.with_(R=2, E=8, K=3, S=10, B=4)])
+def test_failed_plan_and_the_steps_after_it(shape):
+    from oracle.plan import STATUS_BAD_ID, STATUS_UNBALANCED, failed_plan
+    cfg = cfg_of(shape)
+    ids = _bad_ids(shape)
+    with pytest.raises(ValueError):
+        make_plan(ids, cfg)
+    fp = failed_plan(ids, cfg)
+    # counts over the valid ids only, by brute force
+    for e in range(shape.E):
+        assert fp.counts[e] == sum(1 for v in ids.reshape(-1) if v == e)
+    assert fp.counts.sum() == ids.size - 2
+    for r in range(shape.R):
+        assert fp.load0[r] == sum(fp.counts[r * cfg.n:(r + 1) * cfg.n])
+    assert fp.status == STATUS_BAD_ID | STATUS_UNBALANCED
+    assert np.all(fp.route == -1) and not fp.cu_seqlens.any() and np.all(fp.slot_expert == -1)
+    assert len(fp.fills) == 0 and fp.moves.shape == (0, 4)
+    assert not fp.n_redundant.any() and np.all(fp.src_rank == -1)
+    g = np.random.default_rng(5)
+    x = rand_bits(g, (shape.tokens, shape.H))
+    w = rand_bits(g, (shape.E, shape.H, shape.Hp))
+    y = rand_bits(g, (shape.R * shape.SK, shape.Hp))
+    gates = g.random((shape.tokens, shape.K)).astype(np.float32)
+    # nothing is placed, so nothing is written
+    assert not dataflow.dispatch(x, fp, cfg).any()
+    assert not dataflow.prefetch(w, fp, cfg).any()
+    assert not dataflow.grouped_gemm(dataflow.dispatch(x, fp, cfg), w,
+                                     np.zeros((shape.R, shape.B, shape.H, shape.Hp), np.uint16),
+                                     fp, cfg).any()
+    # sums over no routes are zero
+    assert not dataflow.combine(y, gates, fp, cfg).any()
+    assert not dataflow.dispatch_backward(rand_bits(g, (shape.R * shape.SK, shape.H)), fp,
+                                          cfg).any()
+    dy, dg = dataflow.combine_backward(rand_bits(g, (shape.tokens, shape.Hp)), y, gates, fp, cfg)
+    assert not dy.any() and not dg.any()
+    # every home segment is empty: zero gradients; no slot holds an expert
+    gh, gp = dataflow.wgrad(rand_bits(g, (shape.R * shape.SK, shape.H)), y, fp, cfg)
+    assert not gh.any() and not gp.any()
+    h0 = g.standard_normal((shape.E, 2, 3))
+    p0 = g.standard_normal((shape.R, shape.B, 2, 3))
+    h1, p1 = dataflow.reduce_grad(h0, p0, fp, cfg)
+    assert np.array_equal(h1, h0) and np.array_equal(p1, p0)
+    assert np.all(dataflow.route_encode(fp, cfg) == dataflow.NO_DEST)
+    toks = np.arange(shape.tokens)
+    assert not dataflow.combine_tokens(toks, y, gates, fp, cfg).any()
+    assert np.all(dataflow.route_encode_tokens(toks, fp, cfg) == dataflow.NO_DEST)
