@@ -63,8 +63,15 @@
  *    host before anything is launched (bad configuration, null pointer, a
  *    size beyond the documented limits) or reported by the HIP launch;
  *  - conditions only the device can see (expert ids outside [0, E)) set bits
- *    in plan->status instead, and every later step of that plan then leaves
- *    its outputs untouched where the route is -1;
+ *    in plan->status instead.  Such a plan is empty: every route is -1,
+ *    cu_seqlens is all zero and no prefetch slot holds an expert.  Every
+ *    later step of that plan then follows its own definition with no routes
+ *    and no segments: what a route, a segment or a slot addresses is not
+ *    written (xperm, y, dy, dxperm, act, h13, w_pref, grad_pref, and
+ *    reduce_grad changes nothing); sums over a token's routes are empty
+ *    and written as zero (combine's out, dispatch_backward's dx, dgates);
+ *    the weight gradient writes zero to every home row (each home segment
+ *    is empty);
  *  - every bf16 and fp32 tensor argument (and every `workspace`) starts on a
  *    16-byte boundary (the kernels move 16-byte vectors); a misaligned base
  *    is MOE_EINVAL.  torch and hipMalloc allocations are 256-byte aligned;

@@ -146,6 +146,11 @@ def test_dgrad_rank_range_leaves_other_ranks():
 
 
 def test_bench_shape_data_backward():
+    """The data backward at the bench shape in the bench's launch
+    configuration.  Each kernel runs on generated inputs (never on another
+    kernel's output), so every oracle input is independent of the HIP path:
+    combine backward on a generated y and dout, the data-gradient GEMM on a
+    generated dy, dispatch backward on a generated dxperm."""
     shape = W.BENCH
     c, oc = cfgs(shape)
     ids, gates, _, mv = W.routing_zipf(shape, 1.0)
@@ -158,6 +163,8 @@ def test_bench_shape_data_backward():
                          device="cuda")
     y = W.randn_bf16((shape.R * shape.SK, shape.Hp), 72, "cuda")
     dout = W.randn_bf16((shape.tokens, shape.Hp), 73, "cuda")
+    dy_in = W.randn_bf16((shape.R * shape.SK, shape.Hp), 74, "cuda")
+    dxp_in = W.randn_bf16((shape.R * shape.SK, shape.H), 75, "cuda")
     gates_t = torch.from_numpy(gates).cuda()
     dy = torch.empty((shape.R * shape.SK, shape.Hp), dtype=torch.bfloat16, device="cuda")
     dg = torch.empty((shape.tokens, shape.K), device="cuda")
@@ -166,36 +173,31 @@ def test_bench_shape_data_backward():
     ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device="cuda")
     mx.moe_prefetch_weight(c, plan, w_home, w_pref)
     mx.moe_combine_backward(c, plan, dout, y, gates_t, dy, dg)
-    mx.moe_grouped_gemm_dgrad(c, dy, w_home, w_pref, plan.cu_seqlens, dxp, 0, shape.R, ws)
-    mx.moe_dispatch_backward(c, plan, dxp, dx)
+    mx.moe_grouped_gemm_dgrad(c, dy_in, w_home, w_pref, plan.cu_seqlens, dxp, 0, shape.R, ws)
+    mx.moe_dispatch_backward(c, plan, dxp_in, dx)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
-    route = ref.route.reshape(-1, shape.K)
     # combine backward on sampled tokens: dy rows bit-exact, dgates
     toks = np.unique(rng.integers(0, shape.tokens, 256))
-    db = DeviceRows(dout)[toks]
-    kr = route[toks].reshape(-1)
-    yk = DeviceRows(y)[kr]
-    d64 = bf16.bits_to_f64(db)
-    gk = gates[toks].astype(np.float64)
+    q, want_dy, want_dg = dataflow.combine_backward_tokens(toks, DeviceRows(dout), DeviceRows(y),
+                                                           gates, ref, oc)
+    assert (q >= 0).all()
     for k in range(shape.K):
-        want = bf16.f64_to_bits(gk[:, k:k + 1] * d64)
-        got = bits(dy.index_select(0, torch.as_tensor(route[toks, k], device="cuda")))
-        assert np.array_equal(got, want), k
-        ydk = bf16.bits_to_f64(yk[k::shape.K])
-        ref_dg = np.sum(d64 * ydk, axis=1)
-        terms = np.sum(np.abs(d64 * ydk), axis=1)
-        got_dg = dg[torch.as_tensor(toks, device="cuda"), k].cpu().numpy().astype(np.float64)
-        assert np.all(np.abs(got_dg - ref_dg) <= DGATE_TOL * terms + 1e-30), k
-    # data-gradient GEMM on 4096 sampled rows (from the GPU's dy, checked above)
+        got = bits(dy.index_select(0, torch.as_tensor(q[:, k], device="cuda")))
+        assert np.array_equal(got, want_dy[:, k]), k
+    d64 = bf16.bits_to_f64(DeviceRows(dout)[toks])
+    yk = bf16.bits_to_f64(DeviceRows(y)[q.reshape(-1)]).reshape(toks.size, shape.K, -1)
+    terms = np.abs(d64[:, None, :] * yk).sum(axis=2)
+    got_dg = dg.index_select(0, torch.as_tensor(toks, device="cuda")).cpu().numpy()
+    assert np.all(np.abs(got_dg.astype(np.float64) - want_dg) <= DGATE_TOL * terms + 1e-30)
+    # data-gradient GEMM on 4096 sampled rows
     segs = sample_segments(ref, shape, rng, per_rank=6)
     rows = sample_rows(ref, shape, segs, rng, total=4096)
     wr = DeviceRows(w_home)
-    ref_rows = dataflow.dgrad_rows(rows, DeviceRows(dy), wr, OraclePref(wr, ref), ref, oc)
+    ref_rows = dataflow.dgrad_rows(rows, DeviceRows(dy_in), wr, OraclePref(wr, ref), ref, oc)
     worst = rows_close(bits(dxp.index_select(0, torch.as_tensor(rows, device="cuda"))), ref_rows)
     announce("bench dgrad rows", rows.size, "worst rel err", worst)
-    # dispatch backward on sampled tokens, from the GPU's dxperm rows
-    toks = np.unique(rng.integers(0, shape.tokens, 128))
-    xk = bf16.bits_to_f64(DeviceRows(dxp)[route[toks].reshape(-1)])
-    ref_dx = bf16.f64_to_bits(sum(xk[k::shape.K] for k in range(shape.K)))
-    rows_close(bits(dx.index_select(0, torch.as_tensor(toks, device="cuda"))), ref_dx, tol=1e-2)
+    # dispatch backward on sampled tokens
+    toks = np.unique(rng.integers(0, shape.tokens, 512))
+    rows_close(bits(dx.index_select(0, torch.as_tensor(toks, device="cuda"))),
+               dataflow.dispatch_backward_tokens(toks, DeviceRows(dxp_in), ref, oc), tol=1e-2)

@@ -20,7 +20,7 @@ import moe_expert_load_amd as mx
 import workloads as W
 from gpu_helpers import (DeviceRows, announce, assert_plan_equal, bits, cfgs, free, gpu_plan,
                          rows_close)
-from oracle import bf16, dataflow
+from oracle import dataflow
 from oracle.plan import make_plan
 
 pytestmark = pytest.mark.gpu
@@ -71,11 +71,9 @@ def test_gemms_at_the_offset_limit():
         sample |= set(int(v) for v in rng.integers(lo, hi, 200))
     sample = np.array(sorted(sample), np.int64)
     idx = torch.as_tensor(sample, device="cuda")
-    # dispatch: xperm[route[i]] = x[i // K]
-    inv = np.empty(ref.route.size, np.int64)
-    inv[ref.route] = np.arange(ref.route.size)
     xr = DeviceRows(x)
-    assert np.array_equal(bits(xp.index_select(0, idx)), xr[inv[sample] // s.K])
+    assert np.array_equal(bits(xp.index_select(0, idx)),
+                          dataflow.dispatch_rows(sample, xr, ref, oc))
     wr = DeviceRows(w)
     rows_close(bits(y.index_select(0, idx)),
                dataflow.gemm_rows(sample, xr, wr, None, ref, oc))
@@ -96,12 +94,10 @@ def test_gemms_at_the_offset_limit():
     mx.moe_grouped_gemm_wgrad(c, plan, xp, dy, gh, gp, ws)
     torch.cuda.synchronize()
     hs = np.unique(np.concatenate([[0, s.H - 1], rng.integers(0, s.H, 30)]))
-    d64 = bf16.bits_to_f64(bits(dy))
+    hcols = torch.as_tensor(hs, device="cuda")
+    # the sampled h columns of x, as an input of the oracle's sampled form
+    xcols = DeviceRows(x.index_select(1, hcols).contiguous())
     for j in range(s.E):                       # R = 1: both experts are home rows
-        lo, hi = int(cu[j]), int(cu[j + 1])
-        tok = torch.as_tensor(inv[lo:hi] // s.K, device="cuda")
-        hcols = torch.as_tensor(hs, device="cuda")
-        cols = bf16.bits_to_f64(bits(x.index_select(0, tok)[:, hcols]))
-        want = cols.T @ d64[lo:hi]             # G[h, :] = sum_t x[t, h] dy[t, :]
-        got = gh[j][torch.as_tensor(hs, device="cuda")].cpu().numpy()
+        want = dataflow.wgrad_entries(0, j, np.arange(hs.size), xcols, DeviceRows(dy), ref, oc)
+        got = gh[j].index_select(0, hcols).cpu().numpy()
         rows_close(got, want)
