@@ -4,8 +4,9 @@ One step = one pass of the whole path over one batch of synthetic input at
 the bench shape (R=8 virtual ranks, S=8192 tokens/rank, E=384, K=8,
 H=7168, H'=2048, B=E/R=48, bf16, Zipf-biased routing tuned to maxvio 1):
 
-    plan -> prefetch_weight -> dispatch -> grouped GEMM (all 8 ranks, one
-    launch) -> combine -> weight-grad GEMM -> reduce_grad
+    plan (moe_plan_run: the deterministic Theorem-1 construction) ->
+    prefetch_weight -> dispatch -> grouped GEMM (all 8 ranks, one launch) ->
+    combine -> weight-grad GEMM -> reduce_grad
 
 All inputs are resident in HBM before timing starts.  W untimed warmup
 steps, then K timed steps bracketed by device synchronisation; every entry
@@ -13,7 +14,10 @@ point is also bracketed by HIP events on the stream it runs on, giving each
 step's average duration.  After the timed steps the data backward of the
 layer (combine backward -> data-gradient GEMM -> dispatch backward) is timed
 the same way and reported beside the step ("data_backward"), outside
-`value`, and so are the two-projection SwiGLU expert's kernels at the same
+`value`, and so are: the same step with the largest-first planner
+("step_largest_first"); the step at every maxvio of the sweep 0.2 / 1 / 10 /
+20 from one shared seed with both planners ("maxvio_sweep"); the
+two-projection SwiGLU expert's kernels at the same
 shape ("swiglu_expert": first projection [E+B, 7168, 2*2048] fused with
 the activation, second projection [E+B, 2048, 7168], activation backward),
 a two-layer backward sharing one prefetch pool ("prefetch_pool"), one
@@ -27,7 +31,7 @@ all 64 ranks and one rank's grouped GEMM ("large_e").
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--maxvio 1.0]
-                    [--sweep] [--no-cpu-baseline] [--no-extras] [--swiglu-only]
+                    [--no-sweep] [--no-cpu-baseline] [--no-extras] [--swiglu-only]
                     [--vendor-only]
 """
 import argparse
@@ -49,9 +53,19 @@ METRIC = "plan µs + dispatch/combine GB/s + grouped-GEMM TFLOP/s @S8192 E384 K8
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 STEPS = ("plan", "prefetch", "dispatch", "gemm", "combine", "wgrad", "reduce_grad")
-# The step plans with the largest-remaining-first donor policy (the pages'
-# planner is a near-optimal heuristic); both policies are reported.
-PLAN_POLICY = mx.PLAN_LARGEST_FIRST
+# The step plans with the deterministic Theorem-1 construction
+# (moe_plan_run: ascending experts); the largest-remaining-first donor policy
+# is timed beside it.
+PLAN_POLICY = mx.PLAN_ASCENDING
+POLICY_NAMES = {mx.PLAN_ASCENDING: "ascending", mx.PLAN_LARGEST_FIRST: "largest_first"}
+
+
+def run_plan(c, ids, plan, policy):
+    """The planner entry point of a policy: moe_plan_run for the construction
+    as the proof states it, moe_plan_run_policy otherwise."""
+    if policy == mx.PLAN_ASCENDING:
+        return mx.moe_plan_run(c, ids, plan)
+    return mx.moe_plan_run_policy(c, ids, plan, policy)
 
 
 def log(*a):
@@ -222,8 +236,9 @@ def summarize_stats(stats_csv, cmd, out_md):
 class Path:
     """Buffers and calls of one layer at one shape."""
 
-    def __init__(self, shape, ids, gates, seed=0):
+    def __init__(self, shape, ids, gates, seed=0, policy=PLAN_POLICY):
         self.shape = s = shape
+        self.policy = policy
         self.c = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
         dev = "cuda"
         self.ids = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
@@ -262,7 +277,7 @@ class Path:
     def calls(self):
         c, p = self.c, self.plan
         return (
-            ("plan", lambda: mx.moe_plan_run_policy(c, self.ids, p, PLAN_POLICY)),
+            ("plan", lambda: run_plan(c, self.ids, p, self.policy)),
             ("prefetch", lambda: mx.moe_prefetch_weight(c, p, self.w_home, self.w_pref)),
             ("dispatch", lambda: mx.moe_dispatch(c, p, self.x, self.xperm)),
             ("gemm", lambda: mx.moe_grouped_gemm(c, self.xperm, self.w_home, self.w_pref,
@@ -317,80 +332,119 @@ def work_units(shape, plan_views):
     }, {"slots": n_slots, "experts_with_slots": n_cons}
 
 
-def cpu_baseline(shape, ids, gates, path, budget_s=25.0):
-    """The oracle on the host cores, on a bounded sample, scaled to a step."""
-    from threadpoolctl import threadpool_info
+def cpu_baseline(shape, ids, gates, path, policy):
+    """The oracle as it stands, on the host, scaled to one step.
+
+    plan (``oracle.plan.make_plan``) and dispatch (``oracle.dataflow.dispatch``)
+    run at full size; combine runs through the oracle's sampled form on a
+    quarter of the tokens, reduce_grad through ``oracle.dataflow.reduce_grad``
+    on 1/64 of every gradient row (all experts, all slots), the grouped GEMM
+    through ``gemm_rows`` on 4096 sampled rows and the weight gradient through
+    ``wgrad_entries`` on 4 segments x 512 h rows, each extrapolated to the
+    step as stated in ``sample``.  The NumPy element-wise parts run on one
+    thread; the float64 products on BLAS threads (capped at 8).
+    """
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import bf16, dataflow
-    from oracle.plan import POLICY_LARGEST, Cfg, make_plan
+    from oracle.plan import Cfg, make_plan
 
     s = shape
     oc = Cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    t0 = time.perf_counter()
-    ref = make_plan(ids, oc, POLICY_LARGEST if PLAN_POLICY == mx.PLAN_LARGEST_FIRST else 0)
-    t_plan = time.perf_counter() - t0
+    affinity = len(os.sched_getaffinity(0))
+    blas = min(8, affinity)
     rng = np.random.default_rng(0)
-    # dispatch: 2048 tokens, their K rows (the oracle's fancy-index bit copy)
-    toks = np.sort(rng.choice(s.tokens, 2048, replace=False))
-    xb = W.bf16_bits(path.x.index_select(0, torch.as_tensor(toks, device="cuda")))
-    slots = (toks[:, None] * s.K + np.arange(s.K)[None]).reshape(-1)
-    t0 = time.perf_counter()
-    dst = np.argsort(np.argsort(ref.route[slots]))
-    buf = np.zeros((len(slots), s.H), np.uint16)
-    buf[dst] = xb[np.arange(len(slots)) // s.K]
-    t_disp = (time.perf_counter() - t0) * s.tokens / len(toks)
-    # grouped GEMM: oracle gemm_rows on 4 segments x 128 rows; weight
-    # conversion is extrapolated per active segment, the product per row
-    nz = [(r, int(j)) for r in range(s.R) for j in np.nonzero(ref.seg_len[r])[0]]
-    pick = [nz[i] for i in rng.choice(len(nz), 4, replace=False)]
-    wr = _DevRows(path.w_home)
-    xr = _DevRows(path.x)
-    t0 = time.perf_counter()
-    bf16.bits_to_f64(wr[0])
-    t_conv = time.perf_counter() - t0
-    rows = np.concatenate([s.SK * r + ref.cu_seqlens[r, j] +
-                           np.arange(min(128, ref.seg_len[r, j])) for r, j in pick])
-    t0 = time.perf_counter()
-    dataflow.gemm_rows(rows, xr, wr, _OraclePref(wr, ref), ref, oc)
-    t_rows = time.perf_counter() - t0
-    nseg = len(nz)
-    t_gemm = t_conv * nseg + max(t_rows - 4 * t_conv, 0.0) / len(rows) * (s.R * s.SK)
-    # combine: 2048 tokens from synthetic y rows
-    yrows = bf16.f64_to_bits(rng.standard_normal((len(toks) * s.K, s.Hp)))
-    t0 = time.perf_counter()
-    acc = np.zeros((len(toks), s.Hp))
-    for k in range(s.K):
-        acc += gates[toks, k:k + 1].astype(np.float64) * bf16.bits_to_f64(yrows[k::s.K])
-    bf16.f64_to_bits(acc)
-    t_comb = (time.perf_counter() - t0) * s.tokens / len(toks)
-    # weight-grad GEMM: same float64 rate as the forward product (same flops)
-    t_wgrad = t_gemm
-    # reduce_grad: 1/64 of one expert row, scaled to every consumed slot
-    n = s.H * s.Hp // 64
-    hrow = rng.standard_normal(n)
-    prow = rng.standard_normal((2, n))
-    t0 = time.perf_counter()
-    hrow = hrow + prow[0] + prow[1]
-    prow[:] = 0
-    t_red1 = (time.perf_counter() - t0) / 2 * 64
-    n_slots = int((ref.slot_expert >= 0).sum())
-    t_red = t_red1 * n_slots
-    total = t_plan + t_disp + t_gemm + t_comb + t_wgrad + t_red
+    sec, note = {}, {}
+    with threadpool_limits(limits=blas):
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        t0 = time.perf_counter()
+        ref = make_plan(ids, oc, policy)
+        sec["plan"] = time.perf_counter() - t0
+        note["plan"] = "full size"
+        # dispatch at full size, on the step's x copied to the host
+        xb = W.bf16_bits(path.x)
+        t0 = time.perf_counter()
+        dataflow.dispatch(xb, ref, oc)
+        sec["dispatch"] = time.perf_counter() - t0
+        note["dispatch"] = "full size"
+        # combine: a quarter of the tokens, the step's generated dy as y rows
+        yb = W.bf16_bits(path.dy)
+        toks = np.sort(rng.choice(s.tokens, s.tokens // 4, replace=False))
+        t0 = time.perf_counter()
+        dataflow.combine_tokens(toks, yb, gates, ref, oc)
+        sec["combine"] = (time.perf_counter() - t0) * s.tokens / toks.size
+        note["combine"] = "combine_tokens on %d of %d tokens, x%d" % (toks.size, s.tokens,
+                                                                      s.tokens // toks.size)
+        del xb, yb
+        # reduce_grad: every expert and slot, 1/64 of each [H, H'] gradient
+        hs = s.H // 64
+        gh = rng.standard_normal((s.E, hs, s.Hp)).astype(np.float32)
+        gp = rng.standard_normal((s.R, s.B, hs, s.Hp)).astype(np.float32)
+        t0 = time.perf_counter()
+        dataflow.reduce_grad(gh, gp, ref, oc)
+        sec["reduce_grad"] = (time.perf_counter() - t0) * 64
+        note["reduce_grad"] = "reduce_grad on [:, :%d, :] of every gradient, x64" % hs
+        del gh, gp
+        # grouped GEMM: 4096 sampled rows (first and last row of sampled
+        # segments plus seeded rows); the weight conversion is counted once
+        # per active segment, the float64 product per row
+        nz = [(r, int(j)) for r in range(s.R) for j in np.nonzero(ref.seg_len[r])[0]]
+        pick = [nz[i] for i in rng.choice(len(nz), min(48, len(nz)), replace=False)]
+        rows = []
+        for r, j in pick:
+            lo, hi = int(ref.cu_seqlens[r, j]), int(ref.cu_seqlens[r, j + 1])
+            rows += [r * s.SK + lo, r * s.SK + hi - 1]
+        while len(rows) < 4096:
+            r, j = pick[int(rng.integers(len(pick)))]
+            rows.append(r * s.SK + int(rng.integers(ref.cu_seqlens[r, j], ref.cu_seqlens[r, j + 1])))
+        rows = np.unique(np.array(rows, np.int64))
+        wr, xr = _DevRows(path.w_home), _DevRows(path.x)
+        w0 = wr[0]
+        t_conv = min(_timed(lambda: bf16.bits_to_f64(w0)) for _ in range(3))
+        nseg = len(pick)
+        t0 = time.perf_counter()
+        dataflow.gemm_rows(rows, xr, wr, _OraclePref(wr, ref), ref, oc)
+        t_rows = time.perf_counter() - t0
+        per_row = max(t_rows - nseg * t_conv, 0.0) / rows.size
+        sec["gemm"] = t_conv * len(nz) + per_row * s.R * s.SK
+        note["gemm"] = ("gemm_rows on %d rows of %d segments (%.1fs); extrapolated as %d active "
+                        "segments x %.3fs weight conversion + %d rows x %.2fms"
+                        % (rows.size, nseg, t_rows, len(nz), t_conv, s.R * s.SK, per_row * 1e3))
+        # weight gradient: 4 home segments, 512 h rows each
+        home = [(r, j) for r, j in nz if j < s.E]
+        wpick = [home[i] for i in rng.choice(len(home), 4, replace=False)]
+        dr = _DevRows(path.dy)
+        nh = 512
+        t0 = time.perf_counter()
+        nrows = 0
+        for r, j in wpick:
+            hsel = np.sort(rng.choice(s.H, nh, replace=False))
+            dataflow.wgrad_entries(r, j, hsel, xr, dr, ref, oc)
+            nrows += int(ref.seg_len[r, j])
+        t_w = time.perf_counter() - t0
+        sec["wgrad"] = t_w * (s.H / nh) * (s.R * s.SK) / max(nrows, 1)
+        note["wgrad"] = ("wgrad_entries on %d segments (%d rows) x %d of %d h rows (%.1fs); "
+                         "extrapolated per h row and per segment row" % (len(wpick), nrows, nh,
+                                                                         s.H, t_w))
+    total = sum(sec.values())
     return {
         "value": s.tokens / total,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": ("oracle on host: plan at full size (%.2fs); dispatch and combine on 2048 of "
-                   "%d tokens; GEMM via oracle gemm_rows on 4 segments x <=128 rows, weight "
-                   "conversion extrapolated to %d segments and the float64 product per row "
-                   "(fwd and wgrad %.0fs each, extrapolated); reduce_grad on 1/64 of a slot, "
-                   "scaled to %d slots; step total %.1fs extrapolated"
-                   % (t_plan, s.tokens, nseg, t_gemm, n_slots, total)),
-        "seconds": {"plan": t_plan, "dispatch": t_disp, "gemm": t_gemm, "combine": t_comb,
-                    "wgrad": t_wgrad, "reduce_grad": t_red},
-        "host_cpus": {"affinity": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()},
+        "sample": ("oracle on the host, one step extrapolated to %.1fs: " % total +
+                   "; ".join("%s %s (%.2fs)" % (k, note[k], sec[k]) for k in sec)),
+        "seconds": sec,
+        "threads": {"plan": 1, "dispatch": 1, "combine": 1, "reduce_grad": 1,
+                    "gemm": int(blas_threads), "wgrad": int(blas_threads)},
+        "host_cpus": {"affinity": affinity, "cpu_count": os.cpu_count(),
+                      "blas_threads": int(blas_threads)},
     }
+
+
+def _timed(f):
+    t0 = time.perf_counter()
+    f()
+    return time.perf_counter() - t0
 
 
 class _OraclePref:
@@ -408,7 +462,8 @@ class _DevRows:
     def __getitem__(self, i):
         if np.isscalar(i):
             return W.bf16_bits(self.t[int(i)])
-        return W.bf16_bits(self.t.index_select(0, torch.as_tensor(np.asarray(i), device="cuda")))
+        return W.bf16_bits(self.t.index_select(0, torch.as_tensor(np.asarray(i),
+                                                                  device=self.t.device)))
 
 
 def measure(path, steps, warmup):
@@ -427,6 +482,59 @@ def measure(path, steps, warmup):
                  "min": float(np.min(v))} for n, v in per.items() if v}
     span = ev[0][0][1].elapsed_time(ev[-1][-1][2])
     return ms, span / steps, wall / steps * 1e3, stats
+
+
+def step_summary(path, ms, span_ms):
+    """Per-step figures of one measured configuration of the step."""
+    units, st = work_units(path.shape, path.plan.views())
+    v = path.plan.views()
+    status = v["status"].cpu().numpy()
+    out = {"step_ms": span_ms, "ms": ms, "redundant_slots": st["slots"],
+           "max_redundant": int(v["n_redundant"].max().item()), "moves": int(status[1]),
+           "plan_us": ms["plan"] * 1e3}
+    for name in ("prefetch", "dispatch", "combine", "reduce_grad"):
+        out[name + "_GBps"] = units[name][1] / ms[name] / 1e6 if ms[name] > 0 else None
+    for name in ("gemm", "wgrad"):
+        out[name + "_TFLOPs"] = units[name][1] / ms[name] / 1e9
+    return out
+
+
+def measure_policy(path, policy, steps):
+    """The whole step with another planner policy on the same routing; the
+    step's own policy is restored afterwards."""
+    saved = path.policy
+    path.policy = policy
+    ms, span, _, _ = measure(path, steps, 2)
+    out = {"policy": POLICY_NAMES[policy]}
+    out.update(step_summary(path, ms, span))
+    path.policy = saved
+    path.run(1, timed=False)
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_sweep(path, routings, steps):
+    """The whole step at every maxvio of the bench sweep (one shared seed:
+    only the Zipf strength changes), with both planner policies -- the pages'
+    comparison of communication time under growing skew.  Restores the
+    step's routing afterwards."""
+    saved = (path.ids, path.gates, path.policy)
+    out = {}
+    for t, (ids2, gates2, s_bias, mv2) in routings.items():
+        path.ids = torch.from_numpy(np.ascontiguousarray(ids2, np.int32)).cuda()
+        path.gates = torch.from_numpy(np.ascontiguousarray(gates2, np.float32)).cuda()
+        row = {"maxvio": mv2, "zipf_s": s_bias}
+        for p, name in POLICY_NAMES.items():
+            path.policy = p
+            ms, span, _, _ = measure(path, steps, 1)
+            row[name] = step_summary(path, ms, span)
+        out["%g" % t] = row
+        log("sweep", t, {k: (v["step_ms"], v["redundant_slots"]) for k, v in row.items()
+                         if isinstance(v, dict)})
+    path.ids, path.gates, path.policy = saved
+    path.run(1, timed=False)
+    torch.cuda.synchronize()
+    return out
 
 
 def measure_theorem2(path, steps):
@@ -458,7 +566,7 @@ def measure_theorem2(path, steps):
     ci = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, 4, mx.MODE_INFER)
     pi = mx.Plan(ci, dev)
     wpi = path.w_pref[:s.R * 4]
-    calls = (("plan", lambda: mx.moe_plan_run_policy(ci, path.ids, pi, PLAN_POLICY)),
+    calls = (("plan", lambda: run_plan(ci, path.ids, pi, path.policy)),
              ("prefetch", lambda: mx.moe_prefetch_weight(ci, pi, path.w_home, wpi)),
              ("dispatch", lambda: mx.moe_dispatch(ci, pi, path.x, path.xperm)),
              ("gemm", lambda: mx.moe_grouped_gemm(ci, path.xperm, path.w_home, wpi,
@@ -483,7 +591,7 @@ def measure_theorem2(path, steps):
         "n_redundant": v["n_redundant"].cpu().numpy().tolist(),
         "gemm_TFLOPs": units["gemm"][1] / float(np.mean(ts["gemm"])) / 1e9}
     path.ids, path.gates = saved
-    mx.moe_plan_run_policy(path.c, path.ids, path.plan, PLAN_POLICY)
+    run_plan(path.c, path.ids, path.plan, path.policy)
     mx.moe_prefetch_weight(path.c, path.plan, path.w_home, path.w_pref)
     mx.moe_dispatch(path.c, path.plan, path.x, path.xperm)
     torch.cuda.synchronize()
@@ -635,7 +743,7 @@ def measure_pool(path, reps):
           "gh": path.gh}
     w_pool, g_pool, ws = path.w_pref, path.gp, path.ws
     compute, copy = torch.cuda.current_stream(), torch.cuda.Stream()   # default priority
-    mx.moe_plan_run_policy(c, L0["ids"], L0["plan"], PLAN_POLICY)
+    run_plan(c, L0["ids"], L0["plan"], path.policy)
     for L in (L0, L1):
         mx.moe_prefetch_weight(c, L["plan"], L["w"], w_pool)
         mx.moe_dispatch(c, L["plan"], L["x"], L["xperm"])
@@ -817,7 +925,7 @@ def measure_graph(path, reps):
         ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device=dev)
 
         def fwd():
-            mx.moe_plan_run_policy(c, ids_t, plan, PLAN_POLICY)
+            run_plan(c, ids_t, plan, PLAN_POLICY)
             mx.moe_prefetch_weight(c, plan, w, wp)
             mx.moe_dispatch(c, plan, x, xp)
             mx.moe_grouped_gemm(c, xp, w, wp, plan.cu_seqlens, y, 0, s.R, ws)
@@ -861,7 +969,7 @@ def measure_small(reps):
         y = torch.empty((s.R * s.SK, s.Hp), **bf)
         o = torch.empty((s.tokens, s.Hp), **bf)
         ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device=dev)
-        calls = (("plan", lambda: mx.moe_plan_run_policy(c, ids_t, plan, PLAN_POLICY)),
+        calls = (("plan", lambda: run_plan(c, ids_t, plan, PLAN_POLICY)),
                  ("prefetch", lambda: mx.moe_prefetch_weight(c, plan, w, wp)),
                  ("dispatch", lambda: mx.moe_dispatch(c, plan, x, xp)),
                  ("gemm", lambda: mx.moe_grouped_gemm(c, xp, w, wp, plan.cu_seqlens, y, 0, s.R,
@@ -932,8 +1040,8 @@ def measure_large_e(reps):
         ids, gates, _, mv = W.routing_zipf(s, t)
         ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
         g_t = torch.from_numpy(np.ascontiguousarray(gates, np.float32)).to(dev)
-        r_plan = plan_latency(s, t, ids=ids)
-        mx.moe_plan_run_policy(c, ids_t, plan, PLAN_POLICY)
+        r_plan = plan_latency(s, t, ids=ids, maxvio=mv)
+        run_plan(c, ids_t, plan, PLAN_POLICY)
         mx.moe_prefetch_weight(c, plan, w_home, w_pref)
         torch.cuda.synchronize()
         seg = np.diff(plan.views()["cu_seqlens"].cpu().numpy(), axis=1)
@@ -975,23 +1083,24 @@ def measure_backward(path, steps, warmup):
     return {n: float(np.mean(v)) for n, v in per.items()}
 
 
-def plan_latency(shape, target, runs=20, policy=PLAN_POLICY, ids=None):
-    """Plan µs (all four planner launches) at one routing of one shape."""
-    mv = None
+def plan_latency(shape, target, runs=20, policy=PLAN_POLICY, ids=None, maxvio=None):
+    """Plan µs (every planner launch) at one routing of one shape; ``maxvio``
+    is the achieved maxvio of ``ids`` when they are passed in."""
+    mv = maxvio
     if ids is None:
         ids, _, _, mv = W.routing_zipf(shape, target)
     c = mx.make_cfg(shape.R, shape.S, shape.E, shape.K, shape.H, shape.Hp, shape.B, shape.mode)
     plan = mx.Plan(c)
     ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     for _ in range(3):
-        mx.moe_plan_run_policy(c, ids_t, plan, policy)
+        run_plan(c, ids_t, plan, policy)
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     ts = []
     for _ in range(runs):
         a.record()
-        mx.moe_plan_run_policy(c, ids_t, plan, policy)
+        run_plan(c, ids_t, plan, policy)
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b) * 1e3)
@@ -1008,8 +1117,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--maxvio", type=float, default=1.0)
-    ap.add_argument("--sweep", action="store_true", help="also time plan/dispatch/gemm/combine "
-                    "at every maxvio of the sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the maxvio sweep (the step "
+                    "with both planner policies at maxvio 0.2 / 1 / 10 / 20)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the blocks after the step's own (small shapes, graph replay, "
@@ -1128,10 +1237,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "bench shape: R=8 virtual ranks, S=8192 tokens/rank, E=384, K=8, "
-                               "H=7168, H'=2048, B=48, train mode, zipf routing maxvio %.3f" % mv,
+                               "H=7168, H'=2048, B=48, train mode, zipf routing maxvio %.3f, "
+                               "planner moe_plan_run (ascending Theorem-1 construction)" % mv,
                    "R": shape.R, "S": shape.S, "E": shape.E, "K": shape.K, "H": shape.H,
                    "Hp": shape.Hp, "B": shape.B, "maxvio": mv, "zipf_s": s_bias,
-                   "redundant_slots": plan_stats["slots"]},
+                   "redundant_slots": plan_stats["slots"], "planner": POLICY_NAMES[PLAN_POLICY]},
         "components": comps,
         "step_ms": ms,
         "step_ms_stats": step_stats,
@@ -1141,21 +1251,28 @@ def main():
     }
     log("HBM ceilings of plain device kernels (context)")
     line["hbm_ceilings"] = measure_ceilings()
+    log("the step with the largest-first planner")
+    line["step_largest_first"] = measure_policy(path, mx.PLAN_LARGEST_FIRST,
+                                                max(3, args.steps // 2))
     log("planner policies at the bench shape")
+    routings = {t: W.routing_zipf(shape, t) for t in W.MAXVIO_SWEEP["bench"]}
     pol = {}
     for t in W.MAXVIO_SWEEP["bench"]:
-        ids_t2 = W.routing_zipf(shape, t)[0]
+        ids_t2, _, _, mv_t = routings[t]
         pol["maxvio_%g" % t] = {
-            "ascending": plan_latency(shape, t, policy=mx.PLAN_ASCENDING, ids=ids_t2),
-            "largest_first": plan_latency(shape, t, policy=mx.PLAN_LARGEST_FIRST, ids=ids_t2)}
+            name: plan_latency(shape, t, policy=p, ids=ids_t2, maxvio=mv_t)
+            for p, name in POLICY_NAMES.items()}
     line["plan_policies"] = pol
+    if not args.no_sweep:
+        log("maxvio sweep, both planner policies")
+        line["maxvio_sweep"] = measure_sweep(path, routings, max(3, args.steps // 4))
     log("plan latency at the Large-E shape")
     le = {"workload": "Large-E: R=64, S=4096, E=896, K=16, B=14 (plan only)"}
     for t in W.MAXVIO_SWEEP["large_e"]:
-        ids_le = W.routing_zipf(W.LARGE_E, t)[0]
+        ids_le, _, _, mv_le = W.routing_zipf(W.LARGE_E, t)
         le["maxvio_%g" % t] = {
-            "ascending": plan_latency(W.LARGE_E, t, policy=mx.PLAN_ASCENDING, ids=ids_le),
-            "largest_first": plan_latency(W.LARGE_E, t, policy=mx.PLAN_LARGEST_FIRST, ids=ids_le)}
+            name: plan_latency(W.LARGE_E, t, policy=p, ids=ids_le, maxvio=mv_le)
+            for p, name in POLICY_NAMES.items()}
     line["plan_large_e"] = le
     log("data backward")
     bms = measure_backward(path, max(3, args.steps // 2), 1)
@@ -1190,25 +1307,9 @@ def main():
         line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
         log("prefetch pool (two layers, backward)")
         line["prefetch_pool"] = measure_pool(path, 2)
-    if args.sweep:
-        sweep = {}
-        for t in W.MAXVIO_SWEEP["bench"]:
-            ids2, gates2, _, mv2 = W.routing_zipf(shape, t)
-            path.ids = torch.from_numpy(np.ascontiguousarray(ids2, np.int32)).cuda()
-            path.gates = torch.from_numpy(gates2).cuda()
-            m2, _, _, _ = measure(path, max(3, args.steps // 2), 2)
-            u2, st2 = work_units(shape, path.plan.views())
-            sweep["%.1f" % t] = {
-                "maxvio": mv2, "plan_us": m2["plan"] * 1e3,
-                "dispatch_GBps": u2["dispatch"][1] / m2["dispatch"] / 1e6,
-                "combine_GBps": u2["combine"][1] / m2["combine"] / 1e6,
-                "gemm_TFLOPs": u2["gemm"][1] / m2["gemm"] / 1e9,
-                "redundant_slots": st2["slots"]}
-            log("sweep", t, sweep["%.1f" % t])
-        line["maxvio_sweep"] = sweep
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host, bounded sample)")
-        line["cpu_baseline"] = cpu_baseline(shape, ids, gates, path)
+        line["cpu_baseline"] = cpu_baseline(shape, ids, gates, path, PLAN_POLICY)
     if not args.no_extras:
         log("large-E shape (the step's buffers released first)")
         del path
