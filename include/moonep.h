@@ -9,6 +9,7 @@
  *   moe_prefetch_weight  copy redundant experts into prefetch rows [E, E+B)
  *   moe_dispatch         fused permute into expert-grouped [S*K, H] buffers
  *   moe_grouped_gemm     grouped GEMM over the [E+B, H, H'] weight view
+ *   moe_grouped_gemm_noalloc  the same with no workspace argument
  *   moe_combine          gate-weighted unpermute back to tokens
  *   moe_grouped_gemm_wgrad  fp32 weight gradients of the grouped GEMM
  *   moe_reduce_grad      fold prefetch-slot gradients into home rows
@@ -57,7 +58,8 @@
  * Conventions for every entry point:
  *  - every pointer argument is a DEVICE pointer unless stated otherwise, and
  *    the caller allocates and owns it; the library allocates nothing and
- *    keeps no state between calls;
+ *    keeps no state between calls (except the fixed work-list array of
+ *    moe_grouped_gemm_noalloc, described there);
  *  - every call is asynchronous on `stream` and never synchronises the host;
  *  - the return value is MOE_OK or a negative MOE_E* code, detected on the
  *    host before anything is launched (bad configuration, null pointer, a
@@ -249,6 +251,28 @@ int moe_grouped_gemm(const moe_cfg *cfg, const moe_bf16 *xperm,
                      const int32_t *cu_seqlens, moe_bf16 *y,
                      int32_t rank_begin, int32_t rank_end, void *workspace,
                      hipStream_t stream);
+
+/*
+ * Allocation-free moe_grouped_gemm, for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same operation, arguments and results as moe_grouped_gemm
+ * without the `workspace` argument: the work list lives in a fixed device
+ * array of MOE_NOALLOC_SCRATCH_BYTES inside the library (one copy per
+ * device, looked up on the first call on that device and held until the
+ * process ends).  The work list of the listed ranks must fit it:
+ *   256 + 24 * (rank_end - rank_begin) * (ceil(S*K / 256) + E + B)
+ * bytes at most, else MOE_ELIMIT (checked on the host before any launch).
+ * No call allocates or frees anything.  Every call on one device shares
+ * that array, so calls that overlap on one device (on streams with no order
+ * between them) race; calls on one stream are ordered and safe.  Nothing in
+ * the array needs clearing between calls.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_grouped_gemm_noalloc(const moe_cfg *cfg, const moe_bf16 *xperm,
+                             const moe_bf16 *w_home, const moe_bf16 *w_pref,
+                             const int32_t *cu_seqlens, moe_bf16 *y,
+                             int32_t rank_begin, int32_t rank_end,
+                             hipStream_t stream);
 
 /*
  * Gate-weighted combine ("Kimi K3 模型结构（8）", 在线规划、零拷贝、静态 shape:

@@ -21,6 +21,7 @@ PLAN_FIELDS = ("counts", "load0", "route", "cu_seqlens", "slot_expert",
                "n_redundant", "src_rank", "moves", "status", "workspace")
 ENTRY_POINTS = ("moe_plan_sizes", "moe_plan_run", "moe_plan_run_policy", "moe_prefetch_weight",
                 "moe_dispatch", "moe_gemm_workspace_size", "moe_grouped_gemm",
+                "moe_grouped_gemm_noalloc",
                 "moe_combine", "moe_grouped_gemm_wgrad", "moe_reduce_grad",
                 "moe_combine_backward", "moe_grouped_gemm_dgrad",
                 "moe_dispatch_backward", "moe_route_encode", "moe_dispatch_dedup",
@@ -68,6 +69,7 @@ def load(path=None):
         "moe_dispatch": [C, PL, P, P, P],
         "moe_gemm_workspace_size": [C, ctypes.POINTER(SZ)],
         "moe_grouped_gemm": [C, P, P, P, P, P, I32, I32, P, P],
+        "moe_grouped_gemm_noalloc": [C, P, P, P, P, P, I32, I32, P],
         "moe_combine": [C, PL, P, P, P, P],
         "moe_grouped_gemm_wgrad": [C, PL, P, P, P, P, P, P],
         "moe_reduce_grad": [C, PL, P, P, P],
@@ -220,6 +222,20 @@ def moe_grouped_gemm(cfg, xperm, w_home, w_pref, cu_seqlens, y, rank_begin, rank
             _ptr(workspace, torch.uint8, moe_gemm_workspace_size(cfg), "workspace"),
             _stream(stream))
     _check(load().moe_grouped_gemm(*args), "moe_grouped_gemm")
+
+
+def moe_grouped_gemm_noalloc(cfg, xperm, w_home, w_pref, cu_seqlens, y, rank_begin, rank_end,
+                             stream=None):
+    SK = cfg.S * cfg.K
+    hh = cfg.H * cfg.Hp
+    args = (ctypes.byref(cfg),
+            _ptr(xperm, torch.bfloat16, cfg.R * SK * cfg.H, "xperm"),
+            _ptr(w_home, torch.bfloat16, cfg.E * hh, "w_home"),
+            _ptr(w_pref, torch.bfloat16, cfg.R * cfg.B * hh, "w_pref") if cfg.B else None,
+            _ptr(cu_seqlens, torch.int32, cfg.R * (cfg.E + cfg.B + 1), "cu_seqlens"),
+            _ptr(y, torch.bfloat16, cfg.R * SK * cfg.Hp, "y"),
+            int(rank_begin), int(rank_end), _stream(stream))
+    _check(load().moe_grouped_gemm_noalloc(*args), "moe_grouped_gemm_noalloc")
 
 
 def moe_combine(cfg, plan, y, gates, out, stream=None):

@@ -42,6 +42,7 @@
 // reads of the next 16-deep substep are interleaved with the MFMAs of the
 // current one.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -903,7 +904,7 @@ struct SchedArgs {
 
 template <int MODE>
 __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
-  __shared__ int scratch[32];
+  __shared__ int s_part[32];
   __shared__ int s_carry;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int rows = s.E + s.B;
@@ -927,16 +928,16 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
       }
     }
     const int incl = wave_incl_scan(cnt);
-    if (lane == kWave - 1) scratch[wave] = incl;
+    if (lane == kWave - 1) s_part[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-      const int v = lane < 16 ? scratch[lane] : 0;
+      const int v = lane < 16 ? s_part[lane] : 0;
       const int vi = wave_incl_scan(v);
-      if (lane < 16) scratch[lane] = vi - v;
-      if (lane == 15) scratch[16] = vi;
+      if (lane < 16) s_part[lane] = vi - v;
+      if (lane == 15) s_part[16] = vi;
     }
     __syncthreads();
-    const int base = s_carry + scratch[wave] + incl - cnt;
+    const int base = s_carry + s_part[wave] + incl - cnt;
     for (int m = 0; m < cnt; ++m) {
       const int at = base + m;
       if (at < s.cap) {
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
       }
     }
     __syncthreads();
-    if (tid == 0) s_carry += scratch[16];
+    if (tid == 0) s_carry += s_part[16];
     __syncthreads();
   }
   if (tid == 0) *s.nitems = min(s_carry, s.cap);
@@ -1004,6 +1005,56 @@ static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hi
   return hip_status();
 }
 
+// The forward grouped GEMM with its work list in `workspace` (checked).
+static int grouped_gemm_fwd(const moe_cfg* cfg, const moe_bf16* xperm, const moe_bf16* w_home,
+                            const moe_bf16* w_pref, const int32_t* cu_seqlens, moe_bf16* y,
+                            int32_t rank_begin, int32_t rank_end, void* workspace,
+                            hipStream_t stream) {
+  GemmArgs g{};
+  g.xperm = xperm; g.w_home = w_home; g.w_pref = w_pref; g.y = y;
+  g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
+  SchedArgs s{};
+  s.cu = cu_seqlens;
+  s.nitems = reinterpret_cast<int32_t*>(workspace);
+  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
+  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
+  s.SK = cfg->S * cfg->K;
+  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
+  g.items = s.items;
+  g.nitems = s.nitems;
+  return launch_gemm(MODE_FWD, cfg, g, s, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward GEMM.  Its work list (the only scratch the GEMM
+// uses) lives in `scratch`, a file-scope device array of fixed size; each
+// device holds its own copy until the process ends.  In host code the name
+// `scratch` is only a stand-in for the symbol: its device address on each
+// device comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device).
+static int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ELIMIT;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace moonep
 
 using namespace moonep;
@@ -1027,19 +1078,31 @@ extern "C" int moe_grouped_gemm(const moe_cfg* cfg, const moe_bf16* xperm, const
   if (!xperm || !w_home || !cu_seqlens || !y || !workspace) return MOE_EINVAL;
   if (cfg->B > 0 && !w_pref) return MOE_EINVAL;
   if (!aligned16(xperm, w_home, w_pref, y, workspace)) return MOE_EINVAL;
-  GemmArgs g{};
-  g.xperm = xperm; g.w_home = w_home; g.w_pref = w_pref; g.y = y;
-  g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
-  SchedArgs s{};
-  s.cu = cu_seqlens;
-  s.nitems = reinterpret_cast<int32_t*>(workspace);
-  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
-  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
-  s.SK = cfg->S * cfg->K;
-  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
-  g.items = s.items;
-  g.nitems = s.nitems;
-  return launch_gemm(MODE_FWD, cfg, g, s, stream);
+  return grouped_gemm_fwd(cfg, xperm, w_home, w_pref, cu_seqlens, y, rank_begin, rank_end,
+                          workspace, stream);
+}
+
+extern "C" int moe_grouped_gemm_noalloc(const moe_cfg* cfg, const moe_bf16* xperm,
+                                        const moe_bf16* w_home, const moe_bf16* w_pref,
+                                        const int32_t* cu_seqlens, moe_bf16* y,
+                                        int32_t rank_begin, int32_t rank_end,
+                                        hipStream_t stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (rank_begin < 0 || rank_end > cfg->R || rank_begin > rank_end) return MOE_EINVAL;
+  // the work list of the listed ranks must fit the fixed scratch array
+  if (256 + fwd_capacity(cfg, rank_end - rank_begin) * int64_t(sizeof(WorkItem)) >
+      int64_t(MOE_NOALLOC_SCRATCH_BYTES))
+    return MOE_ELIMIT;
+  if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
+  if (!xperm || !w_home || !cu_seqlens || !y) return MOE_EINVAL;
+  if (cfg->B > 0 && !w_pref) return MOE_EINVAL;
+  if (!aligned16(xperm, w_home, w_pref, y)) return MOE_EINVAL;
+  void* ws = nullptr;
+  const int sp = scratch_ptr(&ws);
+  if (sp != MOE_OK) return sp;
+  return grouped_gemm_fwd(cfg, xperm, w_home, w_pref, cu_seqlens, y, rank_begin, rank_end, ws,
+                          stream);
 }
 
 extern "C" int moe_grouped_gemm_swiglu(const moe_cfg* cfg, const moe_bf16* xperm,
