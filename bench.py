@@ -122,12 +122,16 @@ def measured_traffic(kernel):
 
 def _short_kernel(name):
     import re
-    m = re.search(r"moonep::(k_\w+)(<\d+>)?", name)
+    m = re.search(r"moonep::(k_\w+)(?:<(\d+)(?:,\s*(\d+))?>)?", name)
     if m:
-        # k_gemm<MODE> / k_sched<MODE> keep their mode; other templates are
-        # tuning variants of one kernel
-        keep = m.group(1) in ("k_gemm", "k_sched")
-        return m.group(1) + ((m.group(2) or "") if keep else "")
+        # k_gemm<MODE, CLASS> / k_sched<MODE> keep their mode, and k_gemm its
+        # tile class when it is a small one (k_gemm<0>c2: the forward's
+        # class-2 launch); other templates are tuning variants of one kernel
+        k = m.group(1)
+        if k not in ("k_gemm", "k_sched") or m.group(2) is None:
+            return k
+        cls = m.group(3)
+        return "%s<%s>%s" % (k, m.group(2), "c" + cls if cls and cls != "4" else "")
     if name.startswith("Cijk_"):
         # the vendor library's GEMM (comparator only): keep its macro tile
         # and matrix instruction from the kernel name

@@ -259,8 +259,9 @@ int moe_grouped_gemm(const moe_cfg *cfg, const moe_bf16 *xperm,
  * without the `workspace` argument: the work list lives in a fixed device
  * array of MOE_NOALLOC_SCRATCH_BYTES inside the library (one copy per
  * device, looked up on the first call on that device and held until the
- * process ends).  The work list of the listed ranks must fit it:
- *   256 + 24 * (rank_end - rank_begin) * (ceil(S*K / 256) + E + B)
+ * process ends).  The work lists of the listed ranks (one per tile height
+ * class) must fit it:
+ *   256 + 24 * (rank_end - rank_begin) * (ceil(S*K / 256) + 3 * (E + B))
  * bytes at most, else MOE_ELIMIT (checked on the host before any launch).
  * No call allocates or frees anything.  Every call on one device shares
  * that array, so calls that overlap on one device (on streams with no order

@@ -66,6 +66,12 @@ constexpr int BM = 256, BN = 256;
 #endif
 constexpr int kGemmThreads = 256;
 
+// Row-tile A operands interleave the two wave rows by 32-row blocks: wave
+// row wm holds tile rows 64 i + 32 wm + [0, 32), i = 0..3, so a tile with
+// few rows leaves both wave rows equally idle.
+constexpr int kAWaveRow = 32;   // rows between the wave rows
+constexpr int kABlock = 64;     // rows between a wave's row blocks
+
 // Row tiles per band of the column-tile-major work order (a segment of at
 // most this many row tiles is one band).
 #ifndef MOONEP_GEMM_BAND
@@ -90,8 +96,8 @@ struct GemmArgs {
   uint16_t* h13;              // SwiGLU forward: gate and up outputs (optional)
   float* grad_home;
   float* grad_pref;
-  const WorkItem* items;
-  const int32_t* nitems;
+  const WorkItem* items;      // work list of this launch's tile class
+  const int32_t* nitems;      // its item count
   int32_t H, Hp, E, B, SK;
 };
 
@@ -265,8 +271,12 @@ struct GemmTile {
   static constexpr int RPI = 1024 / ROWB;      // row-tile rows per load
 };
 
-template <int MODE>
+// NBK: the tile class of this launch -- tiles of at most 64 NBK rows (4:
+// any tile).  Each class runs as its own persistent launch over its own work
+// list, so each kernel holds one instance of the k-loop.
+template <int MODE, int NBK>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
+  static_assert(NBK == 4 || (MODE != MODE_WGRAD && (NBK == 2 || NBK == 1)), "tile class");
   using T = GemmTile<MODE>;
   constexpr int BK = T::BK, ROWB = T::ROWB, CPR = T::CPR, RSH = T::RSH, NI = T::NI;
   static_assert(NI * 4096 == kTile && (CPR == 4 || CPR == 8), "tile geometry");
@@ -304,14 +314,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     const int c = (4 * j + 2 * (G4 & 1) + ((li & 3) >> 1)) ^ (4 * (li >> 2));
     tr_off[j] = tr_k * 512 + c * 16 + 8 * (li & 1);
   }
-  // Row-tile MFMA reads: row = wm*128 (A) or wn*128 (B) + 32 i + lane%32,
-  // chunk 2 s + lane/32.
+  // Row-tile MFMA reads, chunk 2 s + lane/32.  B (and a k-strided A):
+  // row = wn*128 (wm*128) + 32 i + lane%32.  A row tiles interleave the two
+  // wave rows by 32-row blocks, row = 64 i + 32 wm + lane%32, so a tile
+  // with few rows leaves both wave rows equally idle (see kAStride).
   int ra_off[BK / 16], rb_off[BK / 16];
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) {
     const int row = lane & 31, kc = 2 * s + (lane >> 5);
     const int sw = (kc ^ ((row >> RSH) & (CPR - 1))) << 4;
-    ra_off[s] = (wm * 128 + row) * ROWB + sw;
+    ra_off[s] = (wm * kAWaveRow + row) * ROWB + sw;
     rb_off[s] = (wn * 128 + row) * ROWB + sw;
   }
   // Paired A tile reads: 128-byte rows, 8 chunks swizzled by (row / 2) % 8;
@@ -322,7 +334,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int row = lane & 31, kc = 4 * h + 2 * s + (lane >> 5);
-      rp_off[h][s] = (wm * 128 + row) * 128 + ((kc ^ ((row >> 1) & 7)) << 4);
+      rp_off[h][s] = (wm * kAWaveRow + row) * 128 + ((kc ^ ((row >> 1) & 7)) << 4);
     }
 
   // The work list is read-only here and every index is wave-uniform: read it
@@ -437,316 +449,333 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // Direct loads of k-tile kt into stage S (= kt % kNST).
-    auto issue = [&](auto S_, int kt) {
-      constexpr int S = decltype(S_)::value;
-      unsigned char* As = stage_a<S>();
-      unsigned char* Bs = stage_b<S>();
-      const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
-      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
-#pragma unroll
-      for (int u = 0; u < NI; ++u) {
-        load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
-        load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
-      }
-    };
-    // Half h of those loads (A and B pieces u in [h*NI/2, (h+1)*NI/2)).
-    auto issue_part = [&](auto S_, int kt, int h) {
-      constexpr int S = decltype(S_)::value;
-      unsigned char* As = stage_a<S>();
-      unsigned char* Bs = stage_b<S>();
-      const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
-      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
-#pragma unroll
-      for (int u2 = 0; u2 < NI / 2; ++u2) {
-        const int u = h * (NI / 2) + u2;
-        load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
-        load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
-      }
-    };
-    // Paired mode: B of k-tile kt into stage S; A pair p (k-tiles 2p, 2p+1).
-    auto issue_b = [&](auto S_, int kt) {
-      constexpr int S = decltype(S_)::value;
-      unsigned char* Bs = stage_b<S>();
-      const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
-#pragma unroll
-      for (int u = 0; u < NI; ++u) load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
-    };
-    auto issue_a_pair = [&](int p) {
-      unsigned char* Ap = pair_buf(p);
-      const uint32_t ka = uint32_t(p) * 64 * 2;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) load_lds16(ra, Ap + (wv * 8 + u) * 1024, gop[u], ka);
-    };
-    // Half h of those loads (pieces u in [4h, 4h + 4)).
-    auto issue_a_pair_half = [&](int p, int h) {
-      unsigned char* Ap = pair_buf(p);
-      const uint32_t ka = uint32_t(p) * 64 * 2;
-#pragma unroll
-      for (int u2 = 0; u2 < 4; ++u2) {
-        const int u = 4 * h + u2;
-        load_lds16(ra, Ap + (wv * 8 + u) * 1024, gop[u], ka);
-      }
-    };
-    auto read_frags_pair = [&](auto S_, int kt, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-      constexpr int S = decltype(S_)::value;
-      const unsigned char* Ap = pair_buf(kt >> 1) + rp_off[kt & 1][s];
-      const unsigned char* Bs = stage_b<S>();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ap + i * 32 * 128));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (kRowB) {
-          bfr[j] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Bs + rb_off[s] + j * 32 * ROWB));
-        } else {
-          const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
-          bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
-        }
-      }
-    };
-    // Operand fragments of one 16-deep k substep of stage S.
-    auto read_frags = [&](auto S_, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-      constexpr int S = decltype(S_)::value;
-      const unsigned char* As = stage_a<S>();
-      const unsigned char* Bs = stage_b<S>();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kRowA) {
-          af[i] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * 32 * ROWB));
-        } else {
-          const unsigned char* p = As + tr_off[i] + wm * 256 + s * 16 * 512;
-          af[i] = join(lds_tr(p), lds_tr(p + 4 * 512));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (kRowB) {
-          bfr[j] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Bs + rb_off[s] + j * 32 * ROWB));
-        } else {
-          const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
-          bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
-        }
-      }
-    };
-    // One row of MFMA blocks (A fragment i against the 4 B fragments).
-    auto mfma_row = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    };
-    auto mfma16 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    };
-    // Interleave the 16 MFMAs just issued with the LDS reads of the next
-    // fragments: one read between consecutive MFMAs keeps the matrix pipe fed
-    // while the reads are in flight.
-    auto interleave = [&]() {
-      constexpr int NR = (kRowA ? 4 : 8) + (kRowB ? 4 : 8);   // LDS reads per substep
-#pragma unroll
-      for (int x = 0; x < NR; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 - NR, 0);
-    };
-    // Make stage S (k-tile kt) visible to every wave: each wave waits for
-    // its own direct loads of the stage, then the barrier.
-    // At publish(kt) the loads of k-tiles kt+1 .. kt+kNST-2 may stay in flight.
-    auto publish = [&](int kt) {
-      const int after = min(kNST - 2, nk - 1 - kt);
-      if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
-      else if (kNST >= 4 && after >= 2) wait_vm<4 * NI>();
-      else if (kNST >= 3 && after == 1) wait_vm<2 * NI>();
-      else wait_vm<0>();
-      barrier_lds();
-    };
-    // k-tile kt in stage S.  On entry f0 holds its substep-0 fragments.
-    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    auto step = [&](auto S_, int kt) {
-      constexpr int S = decltype(S_)::value;
-      constexpr int SN = (S + 1) % kNST;
-      unsigned char* As = stage_a<S>();
-      if (kRowA && (kt + 1) * BK > KD) {
-        // ragged K: row-tile chunks past the row length hold the next row's
-        // data -- zero them and re-read this substep's fragments
+    // The k-loop for NB active MFMA row blocks per wave (a tile of at most
+    // 64 NB rows): blocks past them are neither read nor multiplied.
+    auto pipeline = [&](auto NB_) {
+      constexpr int NB = decltype(NB_)::value;
+      // Direct loads of k-tile kt into stage S (= kt % kNST).
+      auto issue = [&](auto S_, int kt) {
+        constexpr int S = decltype(S_)::value;
+        unsigned char* As = stage_a<S>();
         unsigned char* Bs = stage_b<S>();
-        wait_vm<0>();
-        barrier_lds();
-        for (int x = tid; x < kTile / 16; x += kGemmThreads) {
-          const int row = x / CPR, phys = x % CPR;
-          const int kc = phys ^ ((row >> RSH) & (CPR - 1));
-          if (kt * BK + kc * 8 >= KD) {
-            *reinterpret_cast<u32x4*>(As + x * 16) = u32x4{0, 0, 0, 0};
-            if (kRowB) *reinterpret_cast<u32x4*>(Bs + x * 16) = u32x4{0, 0, 0, 0};
+        const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+        const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
+  #pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
+          load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
+        }
+      };
+      // Half h of those loads (A and B pieces u in [h*NI/2, (h+1)*NI/2)).
+      auto issue_part = [&](auto S_, int kt, int h) {
+        constexpr int S = decltype(S_)::value;
+        unsigned char* As = stage_a<S>();
+        unsigned char* Bs = stage_b<S>();
+        const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+        const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
+  #pragma unroll
+        for (int u2 = 0; u2 < NI / 2; ++u2) {
+          const int u = h * (NI / 2) + u2;
+          load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
+          load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
+        }
+      };
+      // Paired mode: B of k-tile kt into stage S; A pair p (k-tiles 2p, 2p+1).
+      auto issue_b = [&](auto S_, int kt) {
+        constexpr int S = decltype(S_)::value;
+        unsigned char* Bs = stage_b<S>();
+        const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
+  #pragma unroll
+        for (int u = 0; u < NI; ++u) load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
+      };
+      auto issue_a_pair = [&](int p) {
+        unsigned char* Ap = pair_buf(p);
+        const uint32_t ka = uint32_t(p) * 64 * 2;
+  #pragma unroll
+        for (int u = 0; u < 8; ++u) load_lds16(ra, Ap + (wv * 8 + u) * 1024, gop[u], ka);
+      };
+      // Half h of those loads (pieces u in [4h, 4h + 4)).
+      auto issue_a_pair_half = [&](int p, int h) {
+        unsigned char* Ap = pair_buf(p);
+        const uint32_t ka = uint32_t(p) * 64 * 2;
+  #pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const int u = 4 * h + u2;
+          load_lds16(ra, Ap + (wv * 8 + u) * 1024, gop[u], ka);
+        }
+      };
+      auto read_frags_pair = [&](auto S_, int kt, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+        constexpr int S = decltype(S_)::value;
+        const unsigned char* Ap = pair_buf(kt >> 1) + rp_off[kt & 1][s];
+        const unsigned char* Bs = stage_b<S>();
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < NB)
+            af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ap + i * kABlock * 128));
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (NB == 0) {
+          } else if (kRowB) {
+            bfr[j] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(Bs + rb_off[s] + j * 32 * ROWB));
+          } else {
+            const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
+            bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
           }
         }
-        __syncthreads();
-        read_frags(S_, 0, fa0, fb0);
-      }
-      // substeps 0 .. SUB-2: MFMAs on one fragment set while the next
-      // substep's fragments are read into the other
-      mfma16(fa0, fb0);
-      read_frags(S_, 1, fa1, fb1);
-      interleave();
-      // Second half of the previous stage's refill (k-tile kt + kNST - 1;
-      // its first half went out in the previous step's last substep), so a
-      // stage's loads are spread over two substeps of MFMAs instead of one.
-      // Loads keep their issue order, so publish's in-flight counts hold.
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt > 0 && kt + kNST - 1 < nk)
-        issue_part(std::integral_constant<int, (S + kNST - 1) % kNST>(), kt + kNST - 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SUB == 4) {
-        mfma16(fa1, fb1);
-        read_frags(S_, 2, fa0, fb0);
-        interleave();
-        mfma16(fa0, fb0);
-        read_frags(S_, 3, fa1, fb1);
-        interleave();
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
-      // Last substep: its fragments are in registers, so its 16 MFMAs cover
-      // the hand-over -- publish k-tile kt+1 (all waves are done with stage
-      // S past that barrier), read substep 0 of the next stage (stale and
-      // unused after the last k-tile) and start refilling stage S with
-      // k-tile kt + kNST (the other half follows in the next step's first
-      // substep) -- instead of the matrix pipe idling through it.
-      mfma_row(fa1, fb1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) publish(kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(std::integral_constant<int, SN>(), 0, fa0, fb0);
-      mfma_row(fa1, fb1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + kNST < nk) issue_part(std::integral_constant<int, S>(), kt + kNST, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_row(fa1, fb1, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_row(fa1, fb1, 3);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Paired mode.  Issue order (per wave): A0, B0, B1, A1, B2, B3, A2 before
-    // the loop, then at step kt: B(kt+4), and for odd kt the pair
-    // (kt+1)/2 + 2 (into the buffer of the pair just finished; its second
-    // half goes out in the next step's first substep, before that step's
-    // publish, so the counts below are unchanged).  Loads
-    // complete in order, so at publish(kt+1) everything issued after B(kt+1)
-    // may stay in flight: A(8) + B(4) + B(4) + A(8) = 24 loads for even kt,
-    // B(4) + B(4) + A(8) = 16 for odd kt -- as long as all of them exist
-    // (kt + 4 < nk); near the end everything is waited for.
-    auto publish_pair = [&](int kt1) {
-      const int kt = kt1 - 1;
-      if (kt + 4 < nk) {
-        if ((kt & 1) == 0) wait_vm<24>();
-        else wait_vm<16>();
-      } else {
-        wait_vm<0>();
-      }
-      barrier_lds();
-    };
-    auto step_pair = [&](auto S_, int kt) {
-      constexpr int S = decltype(S_)::value;
-      constexpr int SN = (S + 1) % kNST;
-      if ((kt + 1) * BK > KD) {
-        // ragged K: chunks past the row length hold the next row's data --
-        // zero them (both halves of the pair; B too when it is a row tile)
-        unsigned char* Ap = pair_buf(kt >> 1);
-        unsigned char* Bs = stage_b<S>();
-        wait_vm<0>();
-        barrier_lds();
-        for (int x = tid; x < kPairTile / 16; x += kGemmThreads) {
-          const int row = x / 8, phys = x % 8;
-          const int kc = phys ^ ((row >> 1) & 7);
-          if ((kt >> 1) * 64 + kc * 8 >= KD) *reinterpret_cast<u32x4*>(Ap + x * 16) = u32x4{0, 0, 0, 0};
+      };
+      // Operand fragments of one 16-deep k substep of stage S.
+      auto read_frags = [&](auto S_, int s, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+        constexpr int S = decltype(S_)::value;
+        const unsigned char* As = stage_a<S>();
+        const unsigned char* Bs = stage_b<S>();
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i >= NB) {
+          } else if (kRowA) {
+            af[i] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * kABlock * ROWB));
+          } else {
+            const unsigned char* p = As + tr_off[i] + wm * 256 + s * 16 * 512;
+            af[i] = join(lds_tr(p), lds_tr(p + 4 * 512));
+          }
         }
-        if (kRowB) {
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (NB == 0) {
+          } else if (kRowB) {
+            bfr[j] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(Bs + rb_off[s] + j * 32 * ROWB));
+          } else {
+            const unsigned char* p = Bs + tr_off[j] + wn * 256 + s * 16 * 512;
+            bfr[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
+          }
+        }
+      };
+      // One row of MFMA blocks (A fragment I against the 4 B fragments);
+      // nothing for a row block past this wave's NB active ones.
+      auto mfma_row = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], auto I_) {
+        constexpr int I = decltype(I_)::value;
+        if constexpr (I < NB) {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[I], bfr[j], acc[I][j], 0, 0, 0);
+        }
+      };
+      auto mfma16 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+  #pragma unroll
+        for (int i = 0; i < NB; ++i)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      };
+      // Interleave the 4*NB MFMAs just issued with the LDS reads of the next
+      // fragments: one read between consecutive MFMAs keeps the matrix pipe fed
+      // while the reads are in flight.
+      auto interleave = [&]() {
+        constexpr int NM = 4 * NB;                                    // MFMAs per substep
+        constexpr int NR = NB == 0 ? 0 : (kRowA ? NB : 8) + (kRowB ? 4 : 8);  // LDS reads
+        constexpr int X = NM < NR ? NM : NR;
+  #pragma unroll
+        for (int x = 0; x < X; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        if constexpr (NM > X) __builtin_amdgcn_sched_group_barrier(0x008, NM - X, 0);
+        if constexpr (NR > X) __builtin_amdgcn_sched_group_barrier(0x100, NR - X, 0);
+      };
+      // Make stage S (k-tile kt) visible to every wave: each wave waits for
+      // its own direct loads of the stage, then the barrier.
+      // At publish(kt) the loads of k-tiles kt+1 .. kt+kNST-2 may stay in flight.
+      auto publish = [&](int kt) {
+        const int after = min(kNST - 2, nk - 1 - kt);
+        if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
+        else if (kNST >= 4 && after >= 2) wait_vm<4 * NI>();
+        else if (kNST >= 3 && after == 1) wait_vm<2 * NI>();
+        else wait_vm<0>();
+        barrier_lds();
+      };
+      // k-tile kt in stage S.  On entry f0 holds its substep-0 fragments.
+      bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+      auto step = [&](auto S_, int kt) {
+        constexpr int S = decltype(S_)::value;
+        constexpr int SN = (S + 1) % kNST;
+        unsigned char* As = stage_a<S>();
+        if (kRowA && (kt + 1) * BK > KD) {
+          // ragged K: row-tile chunks past the row length hold the next row's
+          // data -- zero them and re-read this substep's fragments
+          unsigned char* Bs = stage_b<S>();
+          wait_vm<0>();
+          barrier_lds();
           for (int x = tid; x < kTile / 16; x += kGemmThreads) {
             const int row = x / CPR, phys = x % CPR;
             const int kc = phys ^ ((row >> RSH) & (CPR - 1));
-            if (kt * BK + kc * 8 >= KD) *reinterpret_cast<u32x4*>(Bs + x * 16) = u32x4{0, 0, 0, 0};
+            if (kt * BK + kc * 8 >= KD) {
+              *reinterpret_cast<u32x4*>(As + x * 16) = u32x4{0, 0, 0, 0};
+              if (kRowB) *reinterpret_cast<u32x4*>(Bs + x * 16) = u32x4{0, 0, 0, 0};
+            }
           }
+          __syncthreads();
+          read_frags(S_, 0, fa0, fb0);
         }
-        __syncthreads();
-        read_frags_pair(S_, kt, 0, fa0, fb0);
-      }
-      mfma16(fa0, fb0);
-      read_frags_pair(S_, kt, 1, fa1, fb1);
-      interleave();
-      // Second half of the A pair whose first half the previous (odd) step
-      // issued: same issue order, so publish_pair's in-flight counts hold.
-      __builtin_amdgcn_sched_barrier(0);
-      if (!(kt & 1) && kt > 0 && 2 * (kt / 2 + 2) < nk) issue_a_pair_half(kt / 2 + 2, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
-      mfma_row(fa1, fb1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) publish_pair(kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags_pair(std::integral_constant<int, SN>(), kt + 1, 0, fa0, fb0);
-      mfma_row(fa1, fb1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + kNST < nk) issue_b(std::integral_constant<int, S>(), kt + kNST);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_row(fa1, fb1, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if ((kt & 1) && 2 * ((kt + 1) / 2 + 2) < nk) issue_a_pair_half((kt + 1) / 2 + 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_row(fa1, fb1, 3);
-      __builtin_amdgcn_sched_barrier(0);
-    };
+        // substeps 0 .. SUB-2: MFMAs on one fragment set while the next
+        // substep's fragments are read into the other
+        mfma16(fa0, fb0);
+        read_frags(S_, 1, fa1, fb1);
+        interleave();
+        // Second half of the previous stage's refill (k-tile kt + kNST - 1;
+        // its first half went out in the previous step's last substep), so a
+        // stage's loads are spread over two substeps of MFMAs instead of one.
+        // Loads keep their issue order, so publish's in-flight counts hold.
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt > 0 && kt + kNST - 1 < nk)
+          issue_part(std::integral_constant<int, (S + kNST - 1) % kNST>(), kt + kNST - 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SUB == 4) {
+          mfma16(fa1, fb1);
+          read_frags(S_, 2, fa0, fb0);
+          interleave();
+          mfma16(fa0, fb0);
+          read_frags(S_, 3, fa1, fb1);
+          interleave();
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+        // Last substep: its fragments are in registers, so its 16 MFMAs cover
+        // the hand-over -- publish k-tile kt+1 (all waves are done with stage
+        // S past that barrier), read substep 0 of the next stage (stale and
+        // unused after the last k-tile) and start refilling stage S with
+        // k-tile kt + kNST (the other half follows in the next step's first
+        // substep) -- instead of the matrix pipe idling through it.
+        mfma_row(fa1, fb1, std::integral_constant<int, 0>());
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) publish(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(std::integral_constant<int, SN>(), 0, fa0, fb0);
+        mfma_row(fa1, fb1, std::integral_constant<int, 1>());
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + kNST < nk) issue_part(std::integral_constant<int, S>(), kt + kNST, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_row(fa1, fb1, std::integral_constant<int, 2>());
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_row(fa1, fb1, std::integral_constant<int, 3>());
+        __builtin_amdgcn_sched_barrier(0);
+      };
 
-    if (kPair && nk > 0) {                                      // then nk >= 4
-      issue_a_pair(0);
-      issue_b(std::integral_constant<int, 0>(), 0);
-      issue_b(std::integral_constant<int, 1>(), 1);
-      if (2 < nk) issue_a_pair(1);
-      issue_b(std::integral_constant<int, 2>(), 2);
-      issue_b(std::integral_constant<int, 3>(), 3);
-      if (4 < nk) issue_a_pair(2);
-      // k-tile 0 (A0, B0) has landed once B1, A1, B2, B3, A2 are all that
-      // is left in flight
-      if (nk >= 8) wait_vm<28>();
-      else wait_vm<0>();
-      barrier_lds();
-      read_frags_pair(std::integral_constant<int, 0>(), 0, 0, fa0, fb0);
-      for (int kt = 0; kt < nk; kt += 4) {
-        step_pair(std::integral_constant<int, 0>(), kt);
-        step_pair(std::integral_constant<int, 1>(), kt + 1);
-        step_pair(std::integral_constant<int, 2>(), kt + 2);
-        step_pair(std::integral_constant<int, 3>(), kt + 3);
-      }
-    } else if (nk > 0) {                                        // then nk >= kNST
-    issue(std::integral_constant<int, 0>(), 0);
-    issue(std::integral_constant<int, 1>(), 1);
-    if constexpr (kNST >= 4) {
-      issue(std::integral_constant<int, 2 % kNST>(), 2);
-      issue(std::integral_constant<int, 3 % kNST>(), 3);
-    }
-    if constexpr (kNST == 5) issue(std::integral_constant<int, 4 % kNST>(), 4);
-    // k-tile 0 has landed once the kNST - 1 later k-tiles (2 NI loads each)
-    // are all that is left in flight
-    wait_vm<(kNST - 1) * 2 * NI>();
-    barrier_lds();
-    read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
-    for (int kt = 0; kt < nk; kt += kNST) {
-      step(std::integral_constant<int, 0>(), kt);
-      step(std::integral_constant<int, 1>(), kt + 1);
+      // Paired mode.  Issue order (per wave): A0, B0, B1, A1, B2, B3, A2 before
+      // the loop, then at step kt: B(kt+4), and for odd kt the pair
+      // (kt+1)/2 + 2 (into the buffer of the pair just finished; its second
+      // half goes out in the next step's first substep, before that step's
+      // publish, so the counts below are unchanged).  Loads
+      // complete in order, so at publish(kt+1) everything issued after B(kt+1)
+      // may stay in flight: A(8) + B(4) + B(4) + A(8) = 24 loads for even kt,
+      // B(4) + B(4) + A(8) = 16 for odd kt -- as long as all of them exist
+      // (kt + 4 < nk); near the end everything is waited for.
+      auto publish_pair = [&](int kt1) {
+        const int kt = kt1 - 1;
+        if (kt + 4 < nk) {
+          if ((kt & 1) == 0) wait_vm<24>();
+          else wait_vm<16>();
+        } else {
+          wait_vm<0>();
+        }
+        barrier_lds();
+      };
+      auto step_pair = [&](auto S_, int kt) {
+        constexpr int S = decltype(S_)::value;
+        constexpr int SN = (S + 1) % kNST;
+        if ((kt + 1) * BK > KD) {
+          // ragged K: chunks past the row length hold the next row's data --
+          // zero them (both halves of the pair; B too when it is a row tile)
+          unsigned char* Ap = pair_buf(kt >> 1);
+          unsigned char* Bs = stage_b<S>();
+          wait_vm<0>();
+          barrier_lds();
+          for (int x = tid; x < kPairTile / 16; x += kGemmThreads) {
+            const int row = x / 8, phys = x % 8;
+            const int kc = phys ^ ((row >> 1) & 7);
+            if ((kt >> 1) * 64 + kc * 8 >= KD) *reinterpret_cast<u32x4*>(Ap + x * 16) = u32x4{0, 0, 0, 0};
+          }
+          if (kRowB) {
+            for (int x = tid; x < kTile / 16; x += kGemmThreads) {
+              const int row = x / CPR, phys = x % CPR;
+              const int kc = phys ^ ((row >> RSH) & (CPR - 1));
+              if (kt * BK + kc * 8 >= KD) *reinterpret_cast<u32x4*>(Bs + x * 16) = u32x4{0, 0, 0, 0};
+            }
+          }
+          __syncthreads();
+          read_frags_pair(S_, kt, 0, fa0, fb0);
+        }
+        mfma16(fa0, fb0);
+        read_frags_pair(S_, kt, 1, fa1, fb1);
+        interleave();
+        // Second half of the A pair whose first half the previous (odd) step
+        // issued: same issue order, so publish_pair's in-flight counts hold.
+        __builtin_amdgcn_sched_barrier(0);
+        if (!(kt & 1) && kt > 0 && 2 * (kt / 2 + 2) < nk) issue_a_pair_half(kt / 2 + 2, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+        mfma_row(fa1, fb1, std::integral_constant<int, 0>());
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) publish_pair(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags_pair(std::integral_constant<int, SN>(), kt + 1, 0, fa0, fb0);
+        mfma_row(fa1, fb1, std::integral_constant<int, 1>());
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + kNST < nk) issue_b(std::integral_constant<int, S>(), kt + kNST);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_row(fa1, fb1, std::integral_constant<int, 2>());
+        __builtin_amdgcn_sched_barrier(0);
+        if ((kt & 1) && 2 * ((kt + 1) / 2 + 2) < nk) issue_a_pair_half((kt + 1) / 2 + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_row(fa1, fb1, std::integral_constant<int, 3>());
+        __builtin_amdgcn_sched_barrier(0);
+      };
+
+      if (kPair && nk > 0) {                                      // then nk >= 4
+        issue_a_pair(0);
+        issue_b(std::integral_constant<int, 0>(), 0);
+        issue_b(std::integral_constant<int, 1>(), 1);
+        if (2 < nk) issue_a_pair(1);
+        issue_b(std::integral_constant<int, 2>(), 2);
+        issue_b(std::integral_constant<int, 3>(), 3);
+        if (4 < nk) issue_a_pair(2);
+        // k-tile 0 (A0, B0) has landed once B1, A1, B2, B3, A2 are all that
+        // is left in flight
+        if (nk >= 8) wait_vm<28>();
+        else wait_vm<0>();
+        barrier_lds();
+        read_frags_pair(std::integral_constant<int, 0>(), 0, 0, fa0, fb0);
+        for (int kt = 0; kt < nk; kt += 4) {
+          step_pair(std::integral_constant<int, 0>(), kt);
+          step_pair(std::integral_constant<int, 1>(), kt + 1);
+          step_pair(std::integral_constant<int, 2>(), kt + 2);
+          step_pair(std::integral_constant<int, 3>(), kt + 3);
+        }
+      } else if (nk > 0) {                                        // then nk >= kNST
+      issue(std::integral_constant<int, 0>(), 0);
+      issue(std::integral_constant<int, 1>(), 1);
       if constexpr (kNST >= 4) {
-        step(std::integral_constant<int, 2 % kNST>(), kt + 2);
-        step(std::integral_constant<int, 3 % kNST>(), kt + 3);
+        issue(std::integral_constant<int, 2 % kNST>(), 2);
+        issue(std::integral_constant<int, 3 % kNST>(), 3);
       }
-      if constexpr (kNST == 5) step(std::integral_constant<int, 4 % kNST>(), kt + 4);
-    }
-    }
+      if constexpr (kNST == 5) issue(std::integral_constant<int, 4 % kNST>(), 4);
+      // k-tile 0 has landed once the kNST - 1 later k-tiles (2 NI loads each)
+      // are all that is left in flight
+      wait_vm<(kNST - 1) * 2 * NI>();
+      barrier_lds();
+      read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
+      for (int kt = 0; kt < nk; kt += kNST) {
+        step(std::integral_constant<int, 0>(), kt);
+        step(std::integral_constant<int, 1>(), kt + 1);
+        if constexpr (kNST >= 4) {
+          step(std::integral_constant<int, 2 % kNST>(), kt + 2);
+          step(std::integral_constant<int, 3 % kNST>(), kt + 3);
+        }
+        if constexpr (kNST == 5) step(std::integral_constant<int, 4 % kNST>(), kt + 4);
+      }
+      }
+    };
+    pipeline(std::integral_constant<int, NBK>());
     wait_vm<0>();
     __syncthreads();
 
@@ -797,7 +826,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll 4
         for (int c = lane; c < nout; c += kWave) {
           const int which = c >> 9, rr = (c >> 3) & 63, cc = c & 7;
-          const int m = wm * 128 + half * 64 + rr;
+          const int m = half * 128 + ((rr >> 5) << 6) + wm * kAWaveRow + (rr & 31);
           const int n = a0 + cc * 8;
           const unsigned char* src = which == 0 ? Ca + rr * 144 + cc * 16
                                                 : Cg + (which - 1) * 8192 + rr * 128 + cc * 16;
@@ -849,7 +878,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const int c = lane + kWave * k, rr = c >> 4, cc = c & 15;
-          const int m = wm * 128 + half * 64 + rr;
+          const int m = half * 128 + ((rr >> 5) << 6) + wm * kAWaveRow + (rr & 31);
           const int n = n0 + wn * 128 + cc * 8;
           if (m < it.rows && n < NOUT)
             *reinterpret_cast<u32x4*>(yb + uint32_t(m) * NOUT + n) = piece[k];
@@ -894,26 +923,74 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 // segment of ranks [rb, re), in (rank, weight row, m) order.  Weight
 // gradient: one item per segment that owns a gradient row -- every home row
 // of the rank (empty ones write zeros) and every non-empty prefetch row.
+//
+// Forward-type lists (forward, data gradient, SwiGLU first projection) are
+// split by tile height and the split is chosen per step by a cost model
+// ("Kimi K3 模型结构（8）", rank 内部: expert token counts stay skewed inside a
+// rank, so the GEMM schedule is picked from this step's counts before launch
+// by a time estimate whose key coefficients are tuned offline; "MoonEP :
+// l'équilibrage parfait", 3. Ordonnancement des GEMM d'experts).  On the
+// device, from cu_seqlens and with no host round trip:
+//  * a segment's full row tiles, and a last row tile of more than 128 rows,
+//    go to class 4 (any tile); a last row tile of 65..128 rows to class 2,
+//    of 1..64 rows to class 1 (the data gradient keeps the last tile of a
+//    segment that has full tiles in class 4, beside the tiles it shares a
+//    weight panel with).  Class c runs as its own persistent launch whose
+//    tiles multiply only 2c of their 8 MFMA row blocks;
+//  * a launch over n tiles of class c takes about L + ceil(n / G) t_c on G
+//    workgroups, with t_c = c0 + nk (c1 + c2 c) per tile (nk = k-tiles);
+//  * class 2 is folded into the class-4 list when the rounds it adds there
+//    cost no more than its own launch, and class 1 likewise into the list
+//    of the next larger class that still runs.
+// A folded tail keeps its place right after its segment's other tiles, so
+// each segment's items stay adjacent in every list.
 // ---------------------------------------------------------------------------
 struct SchedArgs {
   const int32_t* cu;
-  WorkItem* items;
-  int32_t* nitems;
-  int32_t rb, re, E, B, n, SK, cap;
+  WorkItem* items;        // class-4 list (weight gradient: its only list)
+  WorkItem* items2;       // class-2 list
+  WorkItem* items1;       // class-1 list
+  int32_t* hdr;           // [0..2] items of the class 4, 2, 1 lists, [3] folds
+                          // (bit 0: class 2 into 4, bit 1: class 1 folded, bit 2:
+                          // into class 4), [4] predicted time in ns
+  int32_t rb, re, E, B, n, SK, cap, cap_s;
+  int32_t G, ntn, nk;     // persistent workgroups, column tiles, k-tiles per tile
+  int32_t c0, c1, c2, cL; // cost model, picoseconds (see above; cL = per launch)
+  int32_t small;          // 1 if the class-2 and class-1 launches run at all
+  int32_t keep_multi;     // 1: the last tile of a multi-tile segment stays in class 4
 };
 
 template <int MODE>
 __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
   __shared__ int s_part[32];
-  __shared__ int s_carry;
+  __shared__ int s_carry[3];
+  __shared__ int s_fold;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int rows = s.E + s.B;
   const int64_t total = int64_t(s.re - s.rb) * rows;
-  if (tid == 0) s_carry = 0;
+  if (tid < 3) s_carry[tid] = 0;
+  if (tid == 0) s_fold = 0;
   __syncthreads();
-  for (int64_t c0 = 0; c0 < total; c0 += 1024) {
-    const int64_t idx = c0 + tid;
-    int cnt = 0, r = 0, j = 0, lo = 0, len = 0;
+  // Block-wide exclusive scan of one value per thread: returns the prefix
+  // and leaves the chunk total in s_part[16].
+  auto block_scan = [&](int v) {
+    const int incl = wave_incl_scan(v);
+    if (lane == kWave - 1) s_part[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+      const int x = lane < 16 ? s_part[lane] : 0;
+      const int xi = wave_incl_scan(x);
+      if (lane < 16) s_part[lane] = xi - x;
+      if (lane == 15) s_part[16] = xi;
+    }
+    __syncthreads();
+    const int pre = s_part[wave] + incl - v;
+    return pre;
+  };
+  // The segment of chunk entry idx: rank, weight row, first row, rows, its
+  // class-4 row tiles and the class (0, 1 or 2) of a separate last tile.
+  auto segment = [&](int64_t idx, int& r, int& j, int& lo, int& len, int& c4, int& tc) {
+    c4 = 0; tc = 0; r = 0; j = 0; lo = 0; len = 0;
     if (idx < total) {
       r = s.rb + (int)(idx / rows);
       j = (int)(idx % rows);
@@ -921,46 +998,109 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
       lo = cu[j];
       len = cu[j + 1] - lo;
       if (MODE == MODE_FWD) {
-        cnt = (len + BM - 1) / BM;
+        const int cnt = (len + BM - 1) / BM;
+        const int tail = len - (cnt - 1) * BM;         // rows of the last row tile
+        tc = cnt == 0 || (s.keep_multi && cnt > 1) ? 0 : tail <= 64 ? 1 : tail <= 128 ? 2 : 0;
+        c4 = cnt - (tc ? 1 : 0);
       } else {
         const bool home = j < s.E && j / s.n == r;
-        cnt = (home || (j >= s.E && len > 0)) ? 1 : 0;
+        c4 = (home || (j >= s.E && len > 0)) ? 1 : 0;
       }
     }
-    const int incl = wave_incl_scan(cnt);
-    if (lane == kWave - 1) s_part[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-      const int v = lane < 16 ? s_part[lane] : 0;
-      const int vi = wave_incl_scan(v);
-      if (lane < 16) s_part[lane] = vi - v;
-      if (lane == 15) s_part[16] = vi;
-    }
-    __syncthreads();
-    const int base = s_carry + s_part[wave] + incl - cnt;
+  };
+  auto write_items = [&](WorkItem* list, int cap, int base, int r, int j, int lo, int len,
+                         int m0, int cnt) {
     for (int m = 0; m < cnt; ++m) {
       const int at = base + m;
-      if (at < s.cap) {
+      if (at < cap) {
         WorkItem w;
         w.r = r;
         w.j = j;
         if (MODE == MODE_FWD) {
-          w.row0 = r * s.SK + lo + m * BM;
-          w.rows = min(BM, len - m * BM);
+          w.row0 = r * s.SK + lo + (m0 + m) * BM;
+          w.rows = min(BM, len - (m0 + m) * BM);
         } else {
           w.row0 = r * s.SK + lo;
           w.rows = len;
         }
         w.first = base;
         w.cnt = cnt;
-        s.items[at] = w;
+        list[at] = w;
+      }
+    }
+  };
+  if (MODE == MODE_FWD) {
+    // Pass 1: row tiles of each class.
+    for (int64_t c0 = 0; c0 < total; c0 += 1024) {
+      int r, j, lo, len, c4, tc;
+      segment(c0 + tid, r, j, lo, len, c4, tc);
+      const int v4 = wave_sum(c4), v2 = wave_sum(tc == 2), v1 = wave_sum(tc == 1);
+      if (lane == 0) {
+        atomicAdd(&s_carry[0], v4);
+        atomicAdd(&s_carry[1], v2);
+        atomicAdd(&s_carry[2], v1);
       }
     }
     __syncthreads();
-    if (tid == 0) s_carry += s_part[16];
+    if (tid == 0) {
+      // the cost model's choice of folds (tile counts = row tiles x ntn)
+      const int64_t G = s.G, n4 = int64_t(s_carry[0]) * s.ntn;
+      const int64_t n2 = int64_t(s_carry[1]) * s.ntn, n1 = int64_t(s_carry[2]) * s.ntn;
+      auto rounds = [&](int64_t x) { return (x + G - 1) / G; };
+      auto tile = [&](int c) { return int64_t(s.c0) + int64_t(s.nk) * (s.c1 + int64_t(s.c2) * c); };
+      auto own = [&](int64_t x, int c) { return x > 0 ? s.cL + rounds(x) * tile(c) : int64_t(0); };
+      const int64_t t4 = tile(4), t2 = tile(2);
+      const bool f2 = n2 > 0 && (!s.small || (rounds(n4 + n2) - rounds(n4)) * t4 <= own(n2, 2));
+      const int64_t m4 = n4 + (f2 ? n2 : 0), m2 = f2 ? 0 : n2;
+      bool f1 = false, to4 = false;
+      if (n1 > 0) {
+        // fold into the smallest class that still runs, if that is cheaper
+        if (!s.small) { f1 = true; to4 = true; }
+        else if (m2 > 0) f1 = (rounds(m2 + n1) - rounds(m2)) * t2 <= own(n1, 1);
+        else { f1 = (rounds(m4 + n1) - rounds(m4)) * t4 <= own(n1, 1); to4 = f1; }
+      }
+      const int64_t e4 = m4 + (to4 ? n1 : 0), e2 = m2 + (f1 && !to4 ? n1 : 0), e1 = f1 ? 0 : n1;
+      const int64_t pred = own(e4, 4) + own(e2, 2) + own(e1, 1);
+      s_fold = (f2 ? 1 : 0) | (f1 ? 2 : 0) | (to4 ? 4 : 0);
+      s.hdr[4] = (int32_t)min<int64_t>(pred / 1000, 0x7fffffff);
+      s_carry[0] = s_carry[1] = s_carry[2] = 0;
+    }
     __syncthreads();
   }
-  if (tid == 0) *s.nitems = min(s_carry, s.cap);
+  const int fold = s_fold;
+  // Pass 2 (the only pass of the weight gradient): the lists, in layout
+  // order; a folded last tile follows its segment's tiles in its new list.
+  for (int64_t c0 = 0; c0 < total; c0 += 1024) {
+    int r, j, lo, len, c4, tc;
+    segment(c0 + tid, r, j, lo, len, c4, tc);
+    // destination list of the last tile: 4, 2 or 1 (0: none)
+    int dst = tc;
+    if (tc == 2 && (fold & 1)) dst = 4;
+    if (tc == 1 && (fold & 2)) dst = (fold & 4) ? 4 : 2;
+    const int a4 = c4 + (dst == 4 ? 1 : 0), a2 = dst == 2 ? 1 : 0, a1 = dst == 1 ? 1 : 0;
+    const int p4 = block_scan(a4);
+    const int t4 = s_part[16];
+    __syncthreads();
+    const int p2 = block_scan(a2);
+    const int t2 = s_part[16];
+    __syncthreads();
+    const int p1 = block_scan(a1);
+    const int t1 = s_part[16];
+    const int b4 = s_carry[0] + p4, b2 = s_carry[1] + p2, b1 = s_carry[2] + p1;
+    write_items(s.items, s.cap, b4, r, j, lo, len, 0, a4);
+    if (a2) write_items(s.items2, s.cap_s, b2, r, j, lo, len, c4, 1);
+    if (a1) write_items(s.items1, s.cap_s, b1, r, j, lo, len, c4, 1);
+    __syncthreads();
+    if (tid == 0) { s_carry[0] += t4; s_carry[1] += t2; s_carry[2] += t1; }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    s.hdr[0] = min(s_carry[0], s.cap);
+    s.hdr[1] = MODE == MODE_FWD ? min(s_carry[1], s.cap_s) : 0;
+    s.hdr[2] = MODE == MODE_FWD ? min(s_carry[2], s.cap_s) : 0;
+    s.hdr[3] = fold;
+    if (MODE != MODE_FWD) s.hdr[4] = 0;
+  }
 }
 
 // Compute units of the current device: the persistent grid's size.  The
@@ -980,28 +1120,98 @@ static int64_t fwd_capacity(const moe_cfg* c, int nranks) {
 
 static int64_t wgrad_capacity(const moe_cfg* c) { return int64_t(c->E) + int64_t(c->R) * c->B; }
 
-static size_t gemm_ws_bytes(const moe_cfg* c) {
-  const int64_t cap = std::max(fwd_capacity(c, c->R), wgrad_capacity(c));
-  return 256 + size_t(cap) * sizeof(WorkItem);
+// Forward-type lists: at most one last tile per segment goes to a small class.
+static int64_t small_capacity(const moe_cfg* c, int nranks) {
+  return int64_t(nranks) * (c->E + c->B);
 }
 
-// The data gradient runs over the forward's work list (the same row tiles).
+// Workspace: a 256-byte header, then the work list (forward-type lists: the
+// class-4, class-2 and class-1 lists).
+static size_t fwd_ws_bytes(const moe_cfg* c, int nranks) {
+  return 256 + size_t(fwd_capacity(c, nranks) + 2 * small_capacity(c, nranks)) * sizeof(WorkItem);
+}
+
+static size_t gemm_ws_bytes(const moe_cfg* c) {
+  return std::max(fwd_ws_bytes(c, c->R), 256 + size_t(wgrad_capacity(c)) * sizeof(WorkItem));
+}
+
+// Cost model of the forward-type schedules, picoseconds: a 256x256 tile of
+// class c (2c of 8 MFMA row blocks) over nk 32-deep k-tiles takes
+// tile + nk (k + k_block c); a persistent launch adds `launch`.  Fitted by
+// moe_expert_load_amd/calibrate.py to forward and data-gradient GEMM times
+// on one MI355X (the SwiGLU projection uses the forward's).
+struct CostModel { int32_t tile, k, k_block, launch; };
+constexpr CostModel kCostFwd = {6119789, 554595, 122365, 0};
+constexpr CostModel kCostDgrad = {6399523, 680492, 83723, 42240708};
+
+// Average rows per home segment, S*K*R/E, below which a step's tails are a
+// large enough share of its tiles for the class-2 and class-1 launches to
+// pay for themselves (measured: decode-size steps gain, steps of about two
+// row tiles per segment lose their launch cost).  The gate depends on the
+// configuration only, so the launch sequence stays static.
+constexpr int64_t kSmallClassRows = 512;
+
+static SchedArgs sched_args(const moe_cfg* c, const int32_t* cu, void* workspace, int rb, int re,
+                            int64_t cap, int64_t cap_s) {
+  SchedArgs s{};
+  s.cu = cu;
+  s.hdr = reinterpret_cast<int32_t*>(workspace);
+  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
+  s.items2 = s.items + cap;
+  s.items1 = s.items2 + cap_s;
+  s.rb = rb; s.re = re; s.E = c->E; s.B = c->B; s.n = c->E / c->R;
+  s.SK = c->S * c->K;
+  s.cap = (int32_t)cap;
+  s.cap_s = (int32_t)cap_s;
+  return s;
+}
+
+static SchedArgs fwd_sched_args(const moe_cfg* c, const int32_t* cu, void* workspace, int rb,
+                                int re) {
+  return sched_args(c, cu, workspace, rb, re, fwd_capacity(c, re - rb), small_capacity(c, re - rb));
+}
+
+template <int MODE>
+static void launch_classes(GemmArgs& g, const SchedArgs& s, int G, hipStream_t stream) {
+  g.items = s.items;
+  g.nitems = s.hdr;
+  hipLaunchKernelGGL((k_gemm<MODE, 4>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+  if (!s.small) return;                  // every tile folded into class 4
+  g.items = s.items2;
+  g.nitems = s.hdr + 1;
+  hipLaunchKernelGGL((k_gemm<MODE, 2>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+  g.items = s.items1;
+  g.nitems = s.hdr + 2;
+  hipLaunchKernelGGL((k_gemm<MODE, 1>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+}
+
+// The data gradient runs over the forward's work lists (the same row tiles).
 static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hipStream_t stream) {
-  if (mode == MODE_WGRAD) {
-    hipLaunchKernelGGL(k_sched<MODE_WGRAD>, dim3(1), dim3(1024), 0, stream, s);
-  } else {
-    hipLaunchKernelGGL(k_sched<MODE_FWD>, dim3(1), dim3(1024), 0, stream, s);
-  }
   int G = num_cus();
   G = std::max(8, G - G % 8);
-  if (mode == MODE_FWD)
-    hipLaunchKernelGGL((k_gemm<MODE_FWD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
-  else if (mode == MODE_SWIGLU)
-    hipLaunchKernelGGL((k_gemm<MODE_SWIGLU>), dim3(G), dim3(kGemmThreads), 0, stream, g);
-  else if (mode == MODE_DGRAD)
-    hipLaunchKernelGGL((k_gemm<MODE_DGRAD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
-  else
-    hipLaunchKernelGGL((k_gemm<MODE_WGRAD>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+  if (mode == MODE_WGRAD) {
+    hipLaunchKernelGGL(k_sched<MODE_WGRAD>, dim3(1), dim3(1024), 0, stream, s);
+    g.items = s.items;
+    g.nitems = s.hdr;
+    hipLaunchKernelGGL((k_gemm<MODE_WGRAD, 4>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+    return hip_status();
+  }
+  const int kdepth = mode == MODE_DGRAD ? c->Hp : c->H;
+  s.G = G;
+  s.ntn = mode == MODE_SWIGLU ? (c->Hp + BN / 2 - 1) / (BN / 2)
+                              : ((mode == MODE_DGRAD ? c->H : c->Hp) + BN - 1) / BN;
+  s.nk = ((kdepth + kBK - 1) / kBK + kNST - 1) / kNST * kNST;
+  const CostModel& m = mode == MODE_DGRAD ? kCostDgrad : kCostFwd;
+  s.c0 = m.tile; s.c1 = m.k; s.c2 = m.k_block; s.cL = m.launch;
+  s.small = int64_t(c->S) * c->K * c->R < kSmallClassRows * c->E ? 1 : 0;
+  // the data gradient's last tile shares its weight panel with the segment's
+  // full tiles in one band: moving it to another launch reads the panel again,
+  // which costs it more than the halved matrix work saves (measured)
+  s.keep_multi = mode == MODE_DGRAD ? 1 : 0;
+  hipLaunchKernelGGL(k_sched<MODE_FWD>, dim3(1), dim3(1024), 0, stream, s);
+  if (mode == MODE_FWD) launch_classes<MODE_FWD>(g, s, G, stream);
+  else if (mode == MODE_SWIGLU) launch_classes<MODE_SWIGLU>(g, s, G, stream);
+  else launch_classes<MODE_DGRAD>(g, s, G, stream);
   return hip_status();
 }
 
@@ -1013,15 +1223,7 @@ static int grouped_gemm_fwd(const moe_cfg* cfg, const moe_bf16* xperm, const moe
   GemmArgs g{};
   g.xperm = xperm; g.w_home = w_home; g.w_pref = w_pref; g.y = y;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
-  SchedArgs s{};
-  s.cu = cu_seqlens;
-  s.nitems = reinterpret_cast<int32_t*>(workspace);
-  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
-  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
-  s.SK = cfg->S * cfg->K;
-  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
-  g.items = s.items;
-  g.nitems = s.nitems;
+  SchedArgs s = fwd_sched_args(cfg, cu_seqlens, workspace, rank_begin, rank_end);
   return launch_gemm(MODE_FWD, cfg, g, s, stream);
 }
 
@@ -1091,8 +1293,7 @@ extern "C" int moe_grouped_gemm_noalloc(const moe_cfg* cfg, const moe_bf16* xper
   if (rc != MOE_OK) return rc;
   if (rank_begin < 0 || rank_end > cfg->R || rank_begin > rank_end) return MOE_EINVAL;
   // the work list of the listed ranks must fit the fixed scratch array
-  if (256 + fwd_capacity(cfg, rank_end - rank_begin) * int64_t(sizeof(WorkItem)) >
-      int64_t(MOE_NOALLOC_SCRATCH_BYTES))
+  if (fwd_ws_bytes(cfg, rank_end - rank_begin) > size_t(MOE_NOALLOC_SCRATCH_BYTES))
     return MOE_ELIMIT;
   if (rank_begin == rank_end || cfg->S == 0) return MOE_OK;
   if (!xperm || !w_home || !cu_seqlens || !y) return MOE_EINVAL;
@@ -1122,15 +1323,7 @@ extern "C" int moe_grouped_gemm_swiglu(const moe_cfg* cfg, const moe_bf16* xperm
   GemmArgs g{};
   g.xperm = xperm; g.w_home = w13_home; g.w_pref = w13_pref; g.y = act; g.h13 = h13;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
-  SchedArgs s{};
-  s.cu = cu_seqlens;
-  s.nitems = reinterpret_cast<int32_t*>(workspace);
-  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
-  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
-  s.SK = cfg->S * cfg->K;
-  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
-  g.items = s.items;
-  g.nitems = s.nitems;
+  SchedArgs s = fwd_sched_args(cfg, cu_seqlens, workspace, rank_begin, rank_end);
   return launch_gemm(MODE_SWIGLU, cfg, g, s, stream);
 }
 
@@ -1148,15 +1341,7 @@ extern "C" int moe_grouped_gemm_dgrad(const moe_cfg* cfg, const moe_bf16* dy, co
   GemmArgs g{};
   g.dy = dy; g.w_home = w_home; g.w_pref = w_pref; g.y = dxperm;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
-  SchedArgs s{};
-  s.cu = cu_seqlens;
-  s.nitems = reinterpret_cast<int32_t*>(workspace);
-  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
-  s.rb = rank_begin; s.re = rank_end; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
-  s.SK = cfg->S * cfg->K;
-  s.cap = (int32_t)fwd_capacity(cfg, rank_end - rank_begin);
-  g.items = s.items;
-  g.nitems = s.nitems;
+  SchedArgs s = fwd_sched_args(cfg, cu_seqlens, workspace, rank_begin, rank_end);
   return launch_gemm(MODE_DGRAD, cfg, g, s, stream);
 }
 
@@ -1172,14 +1357,6 @@ extern "C" int moe_grouped_gemm_wgrad(const moe_cfg* cfg, const moe_plan* plan,
   GemmArgs g{};
   g.xperm = xperm; g.dy = dy; g.grad_home = grad_home; g.grad_pref = grad_pref;
   g.H = cfg->H; g.Hp = cfg->Hp; g.E = cfg->E; g.B = cfg->B; g.SK = cfg->S * cfg->K;
-  SchedArgs s{};
-  s.cu = plan->cu_seqlens;
-  s.nitems = reinterpret_cast<int32_t*>(workspace);
-  s.items = reinterpret_cast<WorkItem*>(reinterpret_cast<char*>(workspace) + 256);
-  s.rb = 0; s.re = cfg->R; s.E = cfg->E; s.B = cfg->B; s.n = cfg->E / cfg->R;
-  s.SK = cfg->S * cfg->K;
-  s.cap = (int32_t)wgrad_capacity(cfg);
-  g.items = s.items;
-  g.nitems = s.nitems;
+  SchedArgs s = sched_args(cfg, plan->cu_seqlens, workspace, 0, cfg->R, wgrad_capacity(cfg), 0);
   return launch_gemm(MODE_WGRAD, cfg, g, s, stream);
 }

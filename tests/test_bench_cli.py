@@ -47,4 +47,7 @@ def test_vendor_kernel_rows_are_named_by_tile():
     name = "Cijk_Ailk_Bljk_BBS_BH_Bias_HA_S_SAV_UserArgs_MT256x256x64_MI16x16x1_SN_LDSB1"
     assert bench._short_kernel(name) == "hipBLASLt Cijk MT256x256x64 MI16x16x1"
     assert bench._short_kernel("void moonep::k_gemm<2>(moonep::GemmArgs)") == "k_gemm<2>"
+    assert bench._short_kernel("void moonep::k_gemm<0, 4>(moonep::GemmArgs)") == "k_gemm<0>"
+    assert bench._short_kernel("void moonep::k_gemm<2, 1>(moonep::GemmArgs)") == "k_gemm<2>c1"
+    assert bench._short_kernel("void moonep::k_sched<0>(moonep::SchedArgs)") == "k_sched<0>"
     assert bench._short_kernel("void moonep::k_route<true>(moonep::PlanArgs)") == "k_route"
