@@ -152,9 +152,11 @@ def summarize_traffic(fetch_csv, write_csv, cmd_fetch, cmd_write):
                 continue
             k = _short_kernel(r["Kernel_Name"])
             if k:
-                acc.setdefault(k, []).append(float(r["Counter_Value"]))
-        # the calibration copy is the largest copyBuffer dispatch
-        return {k: (max(v) if k == "copyBuffer" else sum(v) / len(v)) for k, v in acc.items()}
+                acc.setdefault(k, []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        # the calibration copy (--calibrate-copy) is the first copyBuffer
+        # dispatch of the run; later ones are other blocks' copies
+        return {k: (min(v)[1] if k == "copyBuffer" else sum(x for _, x in v) / len(v))
+                for k, v in acc.items()}
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
     copy_kib = float(1 << 20)                     # the 1 GiB calibration copy
