@@ -998,6 +998,66 @@ def measure_small(reps):
     return out
 
 
+def measure_schedule(reps):
+    """The forward and data-gradient GEMMs where the tile-class schedule
+    acts: the bench's experts (E=384, K=8, H=7168, H'=2048) at decode sizes
+    (S = 256, 1024, 2048 tokens per rank: about 42, 168 and 335 rows per
+    segment) and the skewed shape at maxvio 15, each planned by moe_plan_run
+    from zipf routing (maxvio 1 for the decode sizes).  Reports the median of
+    ``reps`` calls and the scheduler's choice for the step, read from the
+    workspace header: row tiles per class launch (4: any tile, 2: at most
+    128 rows, 1: at most 64 rows), the folds taken and the predicted time.
+    """
+    dev = "cuda"
+    out = {"note": "class 4 tiles multiply all 8 MFMA row blocks, class 2 four, class 1 two; "
+                   "small classes run as their own launches only when segments average under "
+                   "512 rows"}
+    cases = [("decode_S256", W.BENCH.with_(name="decode256", S=256), 1.0),
+             ("decode_S1024", W.BENCH.with_(name="decode1024", S=1024), 1.0),
+             ("decode_S2048", W.BENCH.with_(name="decode2048", S=2048), 1.0),
+             ("skewed_maxvio15", W.SKEWED, 15.0)]
+    for name, s, t in cases:
+        c = mx.make_cfg(s.R, s.S, s.E, s.K, s.H, s.Hp, s.B, s.mode)
+        ids, _, _, mv = W.routing_zipf(s, t)
+        plan = mx.Plan(c, dev)
+        mx.moe_plan_run(c, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev), plan)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        x = W.randn_bf16((s.tokens, s.H), 51, dev)
+        w = W.randn_bf16((s.E, s.H, s.Hp), 52, dev, chunk_rows=1)
+        dy = W.randn_bf16((s.R * s.SK, s.Hp), 53, dev)
+        wp = torch.empty((s.R * s.B, s.H, s.Hp), **bf)
+        xp = torch.empty((s.R * s.SK, s.H), **bf)
+        y = torch.empty((s.R * s.SK, s.Hp), **bf)
+        dxp = torch.empty((s.R * s.SK, s.H), **bf)
+        ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device=dev)
+        mx.moe_prefetch_weight(c, plan, w, wp)
+        mx.moe_dispatch(c, plan, x, xp)
+        fwd = lambda: mx.moe_grouped_gemm(c, xp, w, wp, plan.cu_seqlens, y, 0, s.R, ws)
+        dgr = lambda: mx.moe_grouped_gemm_dgrad(c, dy, w, wp, plan.cu_seqlens, dxp, 0, s.R, ws)
+        tf = _time_calls(fwd, reps)
+        hf = ws[:20].view(torch.int32).cpu().tolist()
+        tb = _time_calls(dgr, reps)
+        hb = ws[:20].view(torch.int32).cpu().tolist()
+        flop = 2.0 * s.H * s.Hp * s.R * s.SK
+        seg = np.diff(plan.views()["cu_seqlens"].cpu().numpy(), axis=1)
+        nseg = int((seg > 0).sum())
+        dec = lambda h: {"class4_row_tiles": h[0], "class2_row_tiles": h[1],
+                         "class1_row_tiles": h[2],
+                         "folded": {"class2_into_4": bool(h[3] & 1), "class1": bool(h[3] & 2),
+                                    "class1_into_4": bool(h[3] & 4)},
+                         "predicted_ms": h[4] * 1e-6}
+        out[name] = {"maxvio": mv, "segments": nseg, "rows_per_segment": s.R * s.SK / nseg,
+                     "forward_ms": tf, "forward_TFLOPs": flop / tf / 1e9,
+                     "forward_weight_GBps": nseg * s.H * s.Hp * 2.0 / tf / 1e6,
+                     "forward_schedule": dec(hf),
+                     "dgrad_ms": tb, "dgrad_TFLOPs": flop / tb / 1e9, "dgrad_schedule": dec(hb)}
+        log("schedule", name, {k: v for k, v in out[name].items() if "schedule" not in k})
+        del x, w, dy, wp, xp, y, dxp, ws, plan
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_large_e(reps):
     """The Large-E shape: R=64 virtual ranks, S=4096, E=896, K=16, H=7168,
     H'=2048, B=14, train mode, zipf maxvio 1 and 10.
@@ -1313,6 +1373,8 @@ def main():
         line["swiglu_expert"] = measure_swiglu(path, max(3, args.steps // 4))
         log("prefetch pool (two layers, backward)")
         line["prefetch_pool"] = measure_pool(path, 2)
+        log("GEMM tile-class schedule at decode sizes and under skew")
+        line["gemm_schedule"] = measure_schedule(10)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host, bounded sample)")
         line["cpu_baseline"] = cpu_baseline(shape, ids, gates, path, PLAN_POLICY)
