@@ -66,6 +66,13 @@ constexpr int BM = 256, BN = 256;
 #endif
 constexpr int kGemmThreads = 256;
 
+// Weight gradient: each XCD owns a contiguous range of items (segments),
+// balanced by predicted time, so all tiles of an item run on one XCD and
+// share its x^T and dy panels in that XCD's L2.
+#ifndef MOONEP_WGRAD_XCD
+#define MOONEP_WGRAD_XCD 1
+#endif
+
 // Row-tile A operands interleave the two wave rows by 32-row blocks: wave
 // row wm holds tile rows 64 i + 32 wm + [0, 32), i = 0..3, so a tile with
 // few rows leaves both wave rows equally idle.
@@ -303,6 +310,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   const int64_t total = int64_t(*g.nitems) * ntm * ntn;
   const int G = gridDim.x, per = G / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  // XCD-owned item ranges (weight gradient): tiles [wbeg, wend) of this XCD
+  constexpr bool kXcdItems = MODE == MODE_WGRAD && MOONEP_WGRAD_XCD;
+  const int64_t wbeg = kXcdItems ? int64_t(g.nitems[8 + xcd]) * ntm * ntn : 0;
+  const int64_t wend = kXcdItems ? int64_t(g.nitems[9 + xcd]) * ntm * ntn : total;
 
   // Per-lane pieces of the transposing reads (col tiles), see lds_tr:
   // G4 = lane/16 picks the k half (G4/2) and the column half (G4%2).
@@ -357,8 +368,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   // fresh array per tile).
   f32x16 acc[4][4];
   for (int64_t q = 0;; ++q) {
-    const int64_t w = q * G + int64_t(xcd) * per + local;
-    if (w >= total) break;
+    const int64_t w = kXcdItems ? wbeg + q * per + local : q * G + int64_t(xcd) * per + local;
+    if (w >= wend) break;
     int tm, tn;
     WorkItem it;
     if (kNMajor) {
@@ -965,11 +976,17 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
   __shared__ int s_part[32];
   __shared__ int s_carry[3];
   __shared__ int s_fold;
+  // weight gradient: predicted time of each item (k-tiles plus a fixed
+  // part) and its exclusive prefix, for the XCD ranges
+  constexpr int kMaxWItems = MODE == MODE_FWD ? 1 : 4096;
+  __shared__ int s_wpre[kMaxWItems], s_wcost[kMaxWItems];
+  __shared__ int s_wcarry, s_xcnt[8];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int rows = s.E + s.B;
   const int64_t total = int64_t(s.re - s.rb) * rows;
   if (tid < 3) s_carry[tid] = 0;
-  if (tid == 0) s_fold = 0;
+  if (tid < 8) s_xcnt[tid] = 0;
+  if (tid == 0) { s_fold = 0; s_wcarry = 0; }
   __syncthreads();
   // Block-wide exclusive scan of one value per thread: returns the prefix
   // and leaves the chunk total in s_part[16].
@@ -1087,6 +1104,17 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
     const int p1 = block_scan(a1);
     const int t1 = s_part[16];
     const int b4 = s_carry[0] + p4, b2 = s_carry[1] + p2, b1 = s_carry[2] + p1;
+    if (MODE == MODE_WGRAD) {
+      // an item's time: its k-tiles (rounded to whole passes of the stage
+      // ring) plus about 12 k-tiles' worth of prologue and fp32 stores
+      const int cost = a4 ? ((len + kBK - 1) / kBK + kNST - 1) / kNST * kNST + 12 : 0;
+      __syncthreads();
+      const int pc = block_scan(cost);
+      const int tc = s_part[16];
+      if (a4 && b4 < kMaxWItems) { s_wpre[b4] = s_wcarry + pc; s_wcost[b4] = cost; }
+      __syncthreads();
+      if (tid == 0) s_wcarry += tc;
+    }
     write_items(s.items, s.cap, b4, r, j, lo, len, 0, a4);
     if (a2) write_items(s.items2, s.cap_s, b2, r, j, lo, len, c4, 1);
     if (a1) write_items(s.items1, s.cap_s, b1, r, j, lo, len, c4, 1);
@@ -1100,6 +1128,29 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
     s.hdr[2] = MODE == MODE_FWD ? min(s_carry[2], s.cap_s) : 0;
     s.hdr[3] = fold;
     if (MODE != MODE_FWD) s.hdr[4] = 0;
+  }
+  if (MODE == MODE_WGRAD) {
+    // XCD x takes the items whose time midpoint falls in [x/8, (x+1)/8) of
+    // the total: contiguous, balanced ranges [hdr[8+x], hdr[9+x])
+    __syncthreads();
+    const int n = min(s_carry[0], s.cap);
+    const int64_t tot = s_wcarry;
+    if (n <= kMaxWItems && tot > 0) {
+      for (int i = tid; i < n; i += 1024) {
+        const int x = (int)min<int64_t>(7, (8 * (2 * int64_t(s_wpre[i]) + s_wcost[i])) / (2 * tot));
+        atomicAdd(&s_xcnt[x], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int acc = 0;
+        for (int x = 0; x < 8; ++x) { s.hdr[8 + x] = acc; acc += s_xcnt[x]; }
+        s.hdr[16] = acc;
+      }
+    } else if (tid == 0) {
+      // no ranges: XCD 0 takes every item (cannot happen within the limits)
+      s.hdr[8] = 0;
+      for (int x = 1; x < 9; ++x) s.hdr[8 + x] = n;
+    }
   }
 }
 
