@@ -401,19 +401,44 @@ __global__ __launch_bounds__(256) void k_reduce_grad(f32x4* __restrict__ grad_ho
   const int ns = s_n;
   if (ns == 0) return;
   f32x4* home = grad_home + int64_t(e) * nvec;
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    f32x4 acc = home[v];
-    for (int s = 0; s < ns; ++s) {
-      f32x4* p = grad_pref + int64_t(s_slot[s]) * nvec + v;
-      const f32x4 g = *p;
-      acc.x += g.x;
-      acc.y += g.y;
-      acc.z += g.z;
-      acc.w += g.w;
-      *p = f32x4{0.f, 0.f, 0.f, 0.f};
+  // U vectors per thread and pass, every load of a slot issued before its
+  // sums, so each thread keeps U (1 + slots) loads in flight; the sum still
+  // runs over ascending ranks per element
+  constexpr int U = 4;
+  const int64_t bd = blockDim.x;
+  const int64_t stride = int64_t(gridDim.x) * bd * U;
+  for (int64_t v0 = int64_t(blockIdx.x) * bd * U + threadIdx.x; v0 < nvec; v0 += stride) {
+    f32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * bd;
+      if (v < nvec) acc[u] = home[v];
     }
-    home[v] = acc;
+    for (int s = 0; s < ns; ++s) {
+      f32x4* p = grad_pref + int64_t(s_slot[s]) * nvec;
+      f32x4 g[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * bd;
+        if (v < nvec) g[u] = p[v];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * bd;
+        if (v < nvec) {
+          acc[u].x += g[u].x;
+          acc[u].y += g[u].y;
+          acc[u].z += g[u].z;
+          acc[u].w += g[u].w;
+          p[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * bd;
+      if (v < nvec) home[v] = acc[u];
+    }
   }
 }
 
@@ -584,7 +609,7 @@ extern "C" int moe_reduce_grad(const moe_cfg* cfg, const moe_plan* plan, float* 
   const PlanLayout L = plan_layout(cfg);
   void* ws = plan->workspace;
   const int64_t nvec = int64_t(cfg->H) * cfg->Hp / 4;
-  int chunks = (int)std::min<int64_t>(128, (nvec + 256 * 8 - 1) / (256 * 8));
+  int chunks = (int)std::min<int64_t>(256, (nvec + 256 * 16 - 1) / (256 * 16));
   if (chunks < 1) chunks = 1;
   hipLaunchKernelGGL(k_reduce_grad, dim3(chunks, cfg->E), dim3(256), 0, stream,
                      reinterpret_cast<f32x4*>(grad_home), reinterpret_cast<f32x4*>(grad_pref),
