@@ -92,13 +92,16 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return __int_as_float(wave_bcast(__float_as_int(v), kWave - 1));
 }
 
+// Lanes without a source (or outside the row mask) see INT_MIN, the identity
+// of max, so each step is one max with a DPP operand.
 __device__ __forceinline__ int wave_max(int v) {
-  v = max(v, MOONEP_DPP(v, v, 0x111, 0xf));
-  v = max(v, MOONEP_DPP(v, v, 0x112, 0xf));
-  v = max(v, MOONEP_DPP(v, v, 0x114, 0xf));
-  v = max(v, MOONEP_DPP(v, v, 0x118, 0xf));
-  v = max(v, MOONEP_DPP(v, v, 0x142, 0xa));
-  v = max(v, MOONEP_DPP(v, v, 0x143, 0xc));
+  constexpr int lo = -2147483647 - 1;
+  v = max(v, MOONEP_DPP(lo, v, 0x111, 0xf));
+  v = max(v, MOONEP_DPP(lo, v, 0x112, 0xf));
+  v = max(v, MOONEP_DPP(lo, v, 0x114, 0xf));
+  v = max(v, MOONEP_DPP(lo, v, 0x118, 0xf));
+  v = max(v, MOONEP_DPP(lo, v, 0x142, 0xa));
+  v = max(v, MOONEP_DPP(lo, v, 0x143, 0xc));
   return wave_bcast(v, kWave - 1);
 }
 

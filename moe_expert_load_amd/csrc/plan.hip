@@ -9,8 +9,9 @@
 // Four launches, all sized from the configuration only:
 //   k_count   C workgroups x 16 waves: per-chunk expert counts (LDS atomics)
 //   k_colscan E/64 workgroups: prefix of the chunk counts over chunks, T_e
-//   k_plan    1 workgroup: loads, the fills (wave 0), cu_seqlens per rank,
-//             per-expert route tables
+//   k_plan    1 workgroup: loads, the fills (wave 0: the loads alone for the
+//             ascending construction, whose moves are then built one
+//             wave per fill), per-rank row prefixes, per-expert route tables
 //   k_route   C workgroups x 16 waves: stable rank of each slot inside its
 //             expert, then its destination row
 #include "common.hpp"
@@ -100,6 +101,52 @@ __device__ int block_excl_scan(int* arr, int n, int* scratch) {
   return total;
 }
 
+// The same over two arrays of n elements at once (one pass, one set of
+// barriers).  Returns the total of a1; *total2 gets the total of a2.
+// scratch needs 34 ints.
+__device__ int block_excl_scan2(int* a1, int* a2, int n, int* scratch, int* total2) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
+  const int b = min(n, tid * per), e = min(n, b + per);
+  int s1 = 0, s2 = 0;
+  for (int i = b; i < e; ++i) {
+    s1 += a1[i];
+    s2 += a2[i];
+  }
+  const int i1 = wave_incl_scan(s1), i2 = wave_incl_scan(s2);
+  if (lane == kWave - 1) {
+    scratch[wave] = i1;
+    scratch[17 + wave] = i2;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int v1 = lane < kRouteWaves ? scratch[lane] : 0;
+    const int v2 = lane < kRouteWaves ? scratch[17 + lane] : 0;
+    const int w1 = wave_incl_scan(v1), w2 = wave_incl_scan(v2);
+    if (lane < kRouteWaves) {
+      scratch[lane] = w1 - v1;
+      scratch[17 + lane] = w2 - v2;
+    }
+    if (lane == kRouteWaves - 1) {
+      scratch[kRouteWaves] = w1;
+      scratch[17 + kRouteWaves] = w2;
+    }
+  }
+  __syncthreads();
+  int r1 = scratch[wave] + i1 - s1, r2 = scratch[17 + wave] + i2 - s2;
+  for (int i = b; i < e; ++i) {
+    const int v1 = a1[i], v2 = a2[i];
+    a1[i] = r1;
+    a2[i] = r2;
+    r1 += v1;
+    r2 += v2;
+  }
+  const int t1 = scratch[kRouteWaves];
+  *total2 = scratch[17 + kRouteWaves];
+  __syncthreads();
+  return t1;
+}
+
 // ---------------------------------------------------------------------------
 // k_colscan: cc[c][e] <- sum of cc[c'][e] over c' < c, and T_e (the counts
 // output).  A workgroup takes 64 experts; its 16 waves split the C chunks.
@@ -166,9 +213,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   int* sOcum = sSpre + R * (B + 1);  // [M] inclusive prefix over overflow moves
   int* sOt = sLoad0;            // [R] overflow rows per rank (after the fills)
   int* sScan = sOcum + M;       // [1024 + 32]
-  __shared__ int sErr, sNm, sNf;
+  __shared__ int sErr, sNm, sNf, sNov;
 
-  if (tid == 0) { sErr = 0; sNm = 0; sNf = 0; }
+  if (tid == 0) { sErr = 0; sNm = 0; sNf = 0; sNov = 0; }
 
   // 1. T_e from k_colscan.
   for (int e = tid; e < E; e += kPlanThreads) sT[e] = a.counts[e];
@@ -205,8 +252,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   // No plan: every rank empty, no moves; k_route writes route = -1.
   auto no_plan = [&]() {
     for (int e = tid; e < E; e += kPlanThreads) { a.counts[e] = sT[e]; a.mcnt[e] = 0; }
-    for (int r = tid; r < R; r += kPlanThreads) {
-      a.load0[r] = sLoad0[r];
+    for (int r = tid; r < R; r += kPlanThreads) {   // load0 is written in step 2
       a.n_red[r] = 0;
       a.src_rank[r] = -1;
     }
@@ -222,28 +268,42 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     return;
   }
 
-  // 3. The fills, on wave 0 (sequential by construction: at most R-1).
-  // Per rank, in registers (rank r in lane r % 64, slot r / 64 of RPL
-  // slots; RPL = 1 up to 64 ranks): its load, its donor cursor (the first
-  // home expert it has not given away entirely) and the slots and moves
-  // already taken from that expert.  A donor gives its experts in
-  // ascending order, so every expert past the cursor is untouched and a
-  // fill reads nothing but T_e; sTaken and sMcnt are only written here.
-  auto fills = [&](auto rpl_tag) {
+  // 3. The fills (sequential by construction: at most R-1).  Each picks the
+  // lowest-id underloaded rank u and the most loaded rank o (lowest id on
+  // ties) and moves SK - load(u) slots of o's home experts to u.  Wave 0
+  // keeps every rank's load in registers (rank r in lane r % 64, slot r / 64
+  // of RPL slots; RPL = 1 up to 64 ranks) and finds u and o with ballots.
+  const bool ascending = a.policy != MOE_PLAN_LARGEST_FIRST;
+  // Ascending construction: a donor gives its home experts in ascending id,
+  // earliest slots first, so its fills take consecutive ranges of one list,
+  // its experts' slots in id order.  The sequential part is then the loads
+  // alone (receiver, donor, amount and where in the donor's list the fill
+  // starts); the moves of every fill follow in parallel from where its range
+  // meets the experts' ranges (step 3b).  Per-fill records, in arrays that
+  // step 5 fills only after the moves are built:
+  int* fNeed = sLoad0;          // [R] slots moved by fill f
+  int* fG = sSpre;              // [R] start of f in its donor's list
+  int* fUD = sScan + 32;        // [R] receiver | donor's fill ordinal << 16
+  int* sFirst = sHpre;          // [E] donor ordinal of the fill that starts e
+  int* sGtot = sHpre + E;       // [R] slots each rank gave away
+  int* sLastD = sOcum;          // [E] donor ordinal of the fill that ends e
+  auto fills_ascending = [&](auto rpl_tag) {
     constexpr int RPL = decltype(rpl_tag)::value;
-    const uint64_t lt = lanemask_lt();
-    int ld[RPL], cur[RPL], ctk[RPL], cmc[RPL];
+    int ld[RPL], gv[RPL], dc[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int r = lane + kWave * i;
       ld[i] = r < R ? sLoad0[r] : 0;
-      cur[i] = r * n;
-      ctk[i] = 0;
-      cmc[i] = 0;
+      gv[i] = 0;                     // slots given so far (as a donor)
+      dc[i] = 0;                     // fills given so far
     }
-    int nm = 0, nf = 0, err = 0;
+    // up to 64 ranks (at most 63 fills) the fill records stay in registers
+    // (fill f in lane f) and are stored after the loop; otherwise lane 0
+    // stores each one as it goes
+    int r_o = 0, r_need = 0, r_g = 0, r_ud = 0, r_recv = -1;
+    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): ld is loaded
+    int nf = 0, err = 0;
     for (int iter = 0; iter < R; ++iter) {
-      // receiver: lowest-id rank that is underloaded now
       int u = -1;
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
@@ -253,7 +313,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
         }
       }
       if (u < 0) break;
-      // donor: largest load, lowest id on ties
       int lb = -1;
 #pragma unroll
       for (int i = 0; i < RPL; ++i)
@@ -268,119 +327,152 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
           if (bal) o = kWave * i + __ffsll((unsigned long long)bal) - 1;
         }
       }
-      int lu = ld[0], co = cur[0], cot = ctk[0], com = cmc[0];
+      int lu = ld[0], go = gv[0], co = dc[0];
 #pragma unroll
       for (int i = 1; i < RPL; ++i) {
         if (i == u / kWave) lu = ld[i];
-        if (i == o / kWave) { co = cur[i]; cot = ctk[i]; com = cmc[i]; }
+        if (i == o / kWave) { go = gv[i]; co = dc[i]; }
       }
       lu = wave_bcast(lu, u % kWave);
+      go = wave_bcast(go, o % kWave);
       co = wave_bcast(co, o % kWave);
-      cot = wave_bcast(cot, o % kWave);
-      com = wave_bcast(com, o % kWave);
+      const int need = SK - lu;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        if (lane + kWave * i == o) { ld[i] -= need; gv[i] += need; dc[i] += 1; }
+        if (lane + kWave * i == u) ld[i] = SK;
+      }
+      if (RPL == 1) {
+        if (lane == nf) { r_o = o; r_need = need; r_g = go; r_ud = u | (co << 16); }
+        if (lane == u) r_recv = nf;
+      } else if (lane == 0) {
+        sFo[nf] = o;
+        fNeed[nf] = need;
+        fG[nf] = go;
+        fUD[nf] = u | (co << 16);
+        sRecv[u] = nf;
+      }
+      ++nf;
+    }
+    if (RPL == 1) {
+      if (lane < nf) {
+        sFo[lane] = r_o;
+        fNeed[lane] = r_need;
+        fG[lane] = r_g;
+        fUD[lane] = r_ud;
+      }
+      if (lane < R) sRecv[lane] = r_recv;
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      if (lane + kWave * i < R) sGtot[lane + kWave * i] = gv[i];
+    if (lane == 0) {
+      sNf = nf;
+      if (err) atomicOr(&sErr, err);
+    }
+  };
+
+  // Largest-first policy: the donor's expert with the most slots still at
+  // home (ties: lowest id), then the next, until the need is met; only the
+  // last one chosen (L) gives part of its slots.  Pass 1 finds L and that
+  // part by selecting in descending order of (remaining, -id); pass 2 walks
+  // the donor's experts in ascending id and moves every expert ranked above
+  // L in full, and L's part.  Moves are written as the fills go.
+  auto fills_largest_first = [&](auto rpl_tag) {
+    constexpr int RPL = decltype(rpl_tag)::value;
+    const uint64_t lt = lanemask_lt();
+    int ld[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int r = lane + kWave * i;
+      ld[i] = r < R ? sLoad0[r] : 0;
+    }
+    int nm = 0, nf = 0, err = 0;
+    for (int iter = 0; iter < R; ++iter) {
+      int u = -1;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        if (u < 0 && kWave * i < R) {
+          const uint64_t bal = __ballot(lane + kWave * i < R && ld[i] < SK);
+          if (bal) u = kWave * i + __ffsll((unsigned long long)bal) - 1;
+        }
+      }
+      if (u < 0) break;
+      int lb = -1;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i)
+        if (lane + kWave * i < R && ld[i] > lb) lb = ld[i];
+      const int mx = wave_max(lb);
+      if (mx <= SK) { err |= MOE_STATUS_INTERNAL; break; }
+      int o = -1;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        if (o < 0 && kWave * i < R) {
+          const uint64_t bal = __ballot(lane + kWave * i < R && ld[i] == mx);
+          if (bal) o = kWave * i + __ffsll((unsigned long long)bal) - 1;
+        }
+      }
+      int lu = ld[0];
+#pragma unroll
+      for (int i = 1; i < RPL; ++i)
+        if (i == u / kWave) lu = ld[i];
+      lu = wave_bcast(lu, u % kWave);
       const int need = SK - lu;
       int d = need;
       const int m0 = nm;
-      int e0 = co;
       const int eend = (o + 1) * n;
-      int ntk = 0, nmc = 0;                     // the new cursor's state
-      if (a.policy == MOE_PLAN_LARGEST_FIRST) {
-        // Largest remaining first: the expert of the donor with the most
-        // slots still at home (ties: lowest id), then the next, until the
-        // need is met; only the last one chosen (L) gives part of its slots.
-        // Pass 1 finds L and that part by selecting in descending order of
-        // (remaining, -id); pass 2 walks the donor's experts in ascending
-        // id and moves every expert ranked above L in full, and L's part.
-        typedef __attribute__((address_space(3))) volatile int lds_vint;
-        lds_vint* vT = (lds_vint*)sT;
-        lds_vint* vTaken = (lds_vint*)sTaken;
-        lds_vint* vMcnt = (lds_vint*)sMcnt;
-        const int eb = o * n;
-        // with at most 64 home experts the donor's remaining counts are read
-        // once into registers (pass 1 does not change them)
-        const int x0 = (n <= kWave && lane < n) ? vT[eb + lane] - vTaken[eb + lane] : 0;
-        int prev_r = 0x7fffffff, prev_e = -1, L = -1, Lr = 0, Lamt = 0;
-        for (int it = 0; it < n && d > 0; ++it) {
-          int best_r = 0, best_e = 0x7fffffff;
-          for (int c0 = eb; c0 < eend; c0 += kWave) {
-            const int e = c0 + lane;
-            int r = -1;
-            if (e < eend) {
-              const int x = n <= kWave ? x0 : vT[e] - vTaken[e];
-              if (x > 0 && (x < prev_r || (x == prev_r && e > prev_e))) r = x;
-            }
-            const int mx = wave_max(r);
-            if (mx <= 0) continue;                                  // uniform
-            const uint64_t bal = __ballot(r == mx);
-            const int ce = c0 + __ffsll((unsigned long long)bal) - 1;
-            if (mx > best_r || (mx == best_r && ce < best_e)) { best_r = mx; best_e = ce; }
-          }
-          if (best_r <= 0) break;
-          if (best_r >= d) { L = best_e; Lr = best_r; Lamt = d; d = 0; }
-          else { d -= best_r; prev_r = best_r; prev_e = best_e; }
-        }
-        if (d > 0 || L < 0) { err |= MOE_STATUS_INTERNAL; break; }
+      typedef __attribute__((address_space(3))) volatile int lds_vint;
+      lds_vint* vT = (lds_vint*)sT;
+      lds_vint* vTaken = (lds_vint*)sTaken;
+      lds_vint* vMcnt = (lds_vint*)sMcnt;
+      const int eb = o * n;
+      // with at most 64 home experts the donor's remaining counts are read
+      // once into registers (pass 1 does not change them)
+      const int x0 = (n <= kWave && lane < n) ? vT[eb + lane] - vTaken[eb + lane] : 0;
+      int prev_r = 0x7fffffff, prev_e = -1, L = -1, Lr = 0, Lamt = 0;
+      for (int it = 0; it < n && d > 0; ++it) {
+        int best_r = 0, best_e = 0x7fffffff;
         for (int c0 = eb; c0 < eend; c0 += kWave) {
           const int e = c0 + lane;
-          int tk = 0, w = 0, take = 0;
+          int r = -1;
           if (e < eend) {
-            tk = vTaken[e];
-            w = vMcnt[e];
-            const int x = vT[e] - tk;
-            if (e == L) take = Lamt;
-            else if (x > 0 && (x > Lr || (x == Lr && e < L))) take = x;
+            const int x = n <= kWave ? x0 : vT[e] - vTaken[e];
+            if (x > 0 && (x < prev_r || (x == prev_r && e > prev_e))) r = x;
           }
-          const uint64_t mvb = __ballot(take > 0);
-          if (take > 0) {
-            const int idx = nm + (int)__popcll(mvb & lt);
-            if (idx < M) { sMe[idx] = e; sMu[idx] = u; sMlo[idx] = tk; sMhi[idx] = tk + take; sMpos[idx] = w; }
-            vTaken[e] = tk + take;
-            vMcnt[e] = w + 1;
-          }
-          nm += (int)__popcll(mvb);
+          const int mx2 = wave_max(r);
+          if (mx2 <= 0) continue;                                  // uniform
+          const uint64_t bal = __ballot(r == mx2);
+          const int ce = c0 + __ffsll((unsigned long long)bal) - 1;
+          if (mx2 > best_r || (mx2 == best_r && ce < best_e)) { best_r = mx2; best_e = ce; }
         }
+        if (best_r <= 0) break;
+        if (best_r >= d) { L = best_e; Lr = best_r; Lamt = d; d = 0; }
+        else { d -= best_r; prev_r = best_r; prev_e = best_e; }
       }
-      // ascending: the donor gives its home experts in ascending id,
-      // earliest slots first
-      while (a.policy != MOE_PLAN_LARGEST_FIRST && d > 0) {
-        if (e0 >= eend) { err |= MOE_STATUS_INTERNAL; break; }
-        const int e = e0 + lane;
-        const bool in = e < eend;
-        const int tt = in ? sT[e] : 0;
-        const int tk = e == co ? cot : 0;
-        const int w = e == co ? com : 0;
-        const int rem = tt - tk;
-        const int incl = wave_incl_scan(rem);
-        const int take = in ? min(max(d - (incl - rem), 0), rem) : 0;
+      if (d > 0 || L < 0) { err |= MOE_STATUS_INTERNAL; break; }
+      for (int c0 = eb; c0 < eend; c0 += kWave) {
+        const int e = c0 + lane;
+        int tk = 0, w = 0, take = 0;
+        if (e < eend) {
+          tk = vTaken[e];
+          w = vMcnt[e];
+          const int x = vT[e] - tk;
+          if (e == L) take = Lamt;
+          else if (x > 0 && (x > Lr || (x == Lr && e < L))) take = x;
+        }
         const uint64_t mvb = __ballot(take > 0);
         if (take > 0) {
           const int idx = nm + (int)__popcll(mvb & lt);
           if (idx < M) { sMe[idx] = e; sMu[idx] = u; sMlo[idx] = tk; sMhi[idx] = tk + take; sMpos[idx] = w; }
-          sTaken[e] = tk + take;
-          sMcnt[e] = w + 1;
+          vTaken[e] = tk + take;
+          vMcnt[e] = w + 1;
         }
         nm += (int)__popcll(mvb);
-        const int tot = wave_bcast(incl, kWave - 1);
-        d -= min(d, tot);
-        if (d == 0) {
-          const uint64_t left = __ballot(in && rem - take > 0);
-          if (left) {
-            const int L = __ffsll((unsigned long long)left) - 1;
-            e0 += L;
-            ntk = wave_bcast(tk + take, L);
-            nmc = wave_bcast(w + (take > 0 ? 1 : 0), L);
-          } else {
-            e0 += kWave;
-          }
-        } else {
-          e0 += kWave;
-        }
       }
-      if (err) break;
       if (nm > M) { err |= MOE_STATUS_INTERNAL; break; }
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
-        if (lane + kWave * i == o) { ld[i] -= need; cur[i] = e0; ctk[i] = ntk; cmc[i] = nmc; }
+        if (lane + kWave * i == o) ld[i] -= need;
         if (lane + kWave * i == u) ld[i] = SK;
       }
       if (lane == 0) {
@@ -398,9 +490,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     }
   };
   if (wave == 0) {
-    if (R <= kWave) fills(IntTag<1>{});
-    else if (R <= 4 * kWave) fills(IntTag<4>{});
-    else fills(IntTag<MOE_MAX_R / kWave>{});
+    if (ascending) {
+      if (R <= kWave) fills_ascending(IntTag<1>{});
+      else if (R <= 4 * kWave) fills_ascending(IntTag<4>{});
+      else fills_ascending(IntTag<MOE_MAX_R / kWave>{});
+    } else {
+      if (R <= kWave) fills_largest_first(IntTag<1>{});
+      else if (R <= 4 * kWave) fills_largest_first(IntTag<4>{});
+      else fills_largest_first(IntTag<MOE_MAX_R / kWave>{});
+    }
   }
   __syncthreads();
   if (sErr & MOE_STATUS_INTERNAL) {
@@ -408,64 +506,234 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     no_plan();
     return;
   }
+
+  // 3b. Ascending construction: the moves of every fill.  Fill f takes the
+  // range [G, G + need) of its donor's list (the donor's home experts' slots
+  // in ascending expert id); every expert of the donor with a slot whose
+  // range meets it gives one move, and the moves of a fill are listed in
+  // ascending expert id after those of the fills before it.  One wave per
+  // fill, one lane per expert of the donor: a prefix sum over the lanes
+  // gives where each expert's slots start in the list, a ballot the moves.
+  if (ascending) {
+    // visit(f, body): calls body(e, p, t, lo, hi, k) on every lane whose
+    // expert e (t slots, starting at p in the donor's list) gives fill f
+    // its in-expert slots [lo, hi); k is the move's index among f's moves;
+    // returns f's move count (every lane)
+    auto visit = [&](int f, auto&& body) {
+      const uint64_t lt = lanemask_lt();
+      const int o = sFo[f], gs = fG[f], ge = gs + fNeed[f];
+      int carry = 0, cnt = 0;
+      for (int c0 = o * n; c0 < (o + 1) * n && carry < ge; c0 += kWave) {
+        const int e = c0 + lane;
+        const int t = e < (o + 1) * n ? sT[e] : 0;
+        const int incl = wave_incl_scan(t);
+        const int p = carry + incl - t;
+        const bool mv = t > 0 && p < ge && p + t > gs;
+        const uint64_t bal = __ballot(mv);
+        if (mv) body(e, p, t, max(gs, p) - p, min(ge, p + t) - p, cnt + (int)__popcll(bal & lt));
+        cnt += (int)__popcll(bal);
+        carry += wave_bcast(incl, kWave - 1);
+      }
+      return cnt;
+    };
+    const int nf = sNf;
+    for (int f = wave; f < nf; f += kRouteWaves) {
+      const int cnt = visit(f, [&](int, int, int, int, int, int) {});
+      if (lane == 0) sFm0[f] = cnt;                  // moves of f, scanned below
+    }
+    __syncthreads();
+    if (wave == 0) {                                 // first and end move of each fill
+      int carry = 0;
+      for (int f0 = 0; f0 < nf; f0 += kWave) {
+        const int f = f0 + lane;
+        const int c = f < nf ? sFm0[f] : 0;
+        const int incl = wave_incl_scan(c);
+        if (f < nf) {
+          sFm0[f] = carry + incl - c;
+          sFm1[f] = carry + incl;
+        }
+        carry += wave_bcast(incl, kWave - 1);
+      }
+      if (lane == 0) {
+        sNm = min(carry, M);
+        if (carry > M) atomicOr(&sErr, MOE_STATUS_INTERNAL);
+      }
+    }
+    __syncthreads();
+    if (sErr & MOE_STATUS_INTERNAL) {
+      no_plan();
+      return;
+    }
+    // An expert's moves come from consecutive fills of its donor, so the
+    // index of a move among its expert's moves is the distance in the
+    // donor's fill order from the fill that takes the expert's first slot,
+    // and the expert's move count that distance for the fill that takes its
+    // last one (its taken slots: all, or up to where the donor stopped
+    // giving).  sMpos holds the donor ordinal until step 4.
+    for (int f = wave; f < nf; f += kRouteWaves) {
+      const int ud = fUD[f], u = ud & 0xffff, d = ud >> 16, m0 = sFm0[f];
+      const int gt = sGtot[sFo[f]];
+      visit(f, [&](int e, int p, int t, int lo, int hi, int k) {
+        const int idx = m0 + k;
+        sMe[idx] = e;
+        sMu[idx] = u;
+        sMlo[idx] = lo;
+        sMhi[idx] = hi;
+        sMpos[idx] = d;
+        if (lo == 0) sFirst[e] = d;
+        const int taken = min(t, gt - p);
+        if (hi == taken) {
+          sLastD[e] = d;
+          sTaken[e] = taken;
+        }
+      });
+    }
+    __syncthreads();
+  }
   const int nm = sNm, nf = sNf;
 
   // 4. Moves per expert in fill order: CSR start of each expert.
-  for (int e = tid; e < E; e += kPlanThreads) sMptr[e] = sMcnt[e];
+  for (int e = tid; e < E; e += kPlanThreads) {
+    if (ascending) sMcnt[e] = sTaken[e] > 0 ? sLastD[e] - sFirst[e] + 1 : 0;
+    sMptr[e] = sMcnt[e];
+  }
+  if (ascending)
+    for (int m = tid; m < nm; m += kPlanThreads) sMpos[m] -= sFirst[sMe[m]];
   __syncthreads();
   block_excl_scan(sMptr, E, sScan);
 
-  // 5. The last wave lists the experts that have moves (for reduce_grad).
-  // Then per rank: prefix of its home row lengths, of its prefetch rows and
-  // of its overflow rows (inference); cu_seqlens follows in closed form.
-  if (wave == kRouteWaves - 1) {
-    const uint64_t lt = lanemask_lt();
-    int k = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const bool has = e0 + lane < E && sMcnt[e0 + lane] > 0;
-      const uint64_t bal = __ballot(has);
-      if (has) a.cons[k + (int)__popcll(bal & lt)] = e0 + lane;
-      k += (int)__popcll(bal);
+  // 5. Per rank: prefix of its home row lengths (over its experts), of its
+  // prefetch rows (over its slots) and of its overflow rows (inference:
+  // over its moves past the B slots); cu_seqlens follows in closed form.
+  // Up to 32 ranks a wave takes a rank at a time (and the last wave lists
+  // the experts that have moves, for reduce_grad); with more ranks the
+  // first two are block-wide scans over all ranks at once (each rank's part
+  // is a difference of the global prefix) with that list compacted in the
+  // same scan.
+  if (R <= 2 * kRouteWaves) {
+    if (wave == kRouteWaves - 1) {
+      const uint64_t lt = lanemask_lt();
+      int k = 0;
+      for (int e0 = 0; e0 < E; e0 += kWave) {
+        const bool has = e0 + lane < E && sMcnt[e0 + lane] > 0;
+        const uint64_t bal = __ballot(has);
+        if (has) a.cons[k + (int)__popcll(bal & lt)] = e0 + lane;
+        k += (int)__popcll(bal);
+      }
+      if (lane == 0) a.misc[0] = k;
     }
-    if (lane == 0) a.misc[0] = k;
+    for (int r = wave; r < R; r += kRouteWaves) {
+      const int f = sRecv[r];
+      const int m0 = f >= 0 ? sFm0[f] : 0, m1 = f >= 0 ? sFm1[f] : 0;
+      const int nred = m1 - m0;
+      int carry = 0;
+      for (int t0 = 0; t0 < n; t0 += kWave) {
+        const int t = t0 + lane;
+        const int len = t < n ? sT[r * n + t] - sTaken[r * n + t] : 0;
+        const int incl = wave_incl_scan(len);
+        if (t < n) sHpre[r * (n + 1) + t] = a.hpre[r * (n + 1) + t] = carry + incl - len;
+        carry += wave_bcast(incl, kWave - 1);
+      }
+      if (lane == 0) sHpre[r * (n + 1) + n] = a.hpre[r * (n + 1) + n] = carry;
+      carry = 0;
+      for (int b0 = 0; b0 < B; b0 += kWave) {
+        const int b = b0 + lane;
+        const int len = (b < B && b < nred) ? sMhi[m0 + b] - sMlo[m0 + b] : 0;
+        const int incl = wave_incl_scan(len);
+        if (b < B) sSpre[r * (B + 1) + b] = a.spre[r * (B + 1) + b] = carry + incl - len;
+        carry += wave_bcast(incl, kWave - 1);
+      }
+      if (lane == 0) sSpre[r * (B + 1) + B] = a.spre[r * (B + 1) + B] = carry;
+      carry = 0;
+      for (int m = m0 + B + lane; m - lane < m1; m += kWave) {     // overflow moves
+        const int len = m < m1 ? sMhi[m] - sMlo[m] : 0;
+        const int incl = wave_incl_scan(len);
+        if (m < m1) sOcum[m] = a.ocum[m] = carry + incl;
+        carry += wave_bcast(incl, kWave - 1);
+      }
+      if (lane == 0) {
+        sOt[r] = carry;
+        a.rinfo[3 * r + 0] = carry;                 // overflow rows
+        a.rinfo[3 * r + 1] = m0 + B;                // overflow moves [m0 + B, m1)
+        a.rinfo[3 * r + 2] = m1;
+      }
+    }
+    __syncthreads();
+  } else {
+    {
+      int* tX = sHpre;               // [E] T - taken, then its global prefix
+      int* tC = sOcum;               // [E] 1 where e has moves, then its prefix
+      const int NH = R * (n + 1), NS = R * (B + 1);
+      for (int e = tid; e < E; e += kPlanThreads) {
+        tX[e] = sT[e] - sTaken[e];
+        tC[e] = sMcnt[e] > 0;
+      }
+      for (int i = tid; i < NS; i += kPlanThreads) {
+        const int r = i / (B + 1), b = i % (B + 1), f = sRecv[r];
+        const int m0 = f >= 0 ? sFm0[f] : 0, nred = f >= 0 ? sFm1[f] - m0 : 0;
+        sSpre[i] = (b < B && b < nred) ? sMhi[m0 + b] - sMlo[m0 + b] : 0;
+      }
+      __syncthreads();
+      int ncons = 0;
+      const int hx = block_excl_scan2(tX, tC, E, sScan, &ncons);
+      block_excl_scan(sSpre, NS, sScan);
+      constexpr int kPer = (MOE_MAX_E + MOE_MAX_R + kPlanThreads - 1) / kPlanThreads;
+      int hv[kPer], sv[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kPlanThreads;
+        if (i < NH) {
+          const int r = i / (n + 1), j = r * n + i % (n + 1);
+          hv[k] = (j < E ? tX[j] : hx) - tX[r * n];
+        }
+        if (i < NS) sv[k] = sSpre[i] - sSpre[(i / (B + 1)) * (B + 1)];
+      }
+      for (int e = tid; e < E; e += kPlanThreads)
+        if (sMcnt[e] > 0) a.cons[tC[e]] = e;
+      if (tid == 0) a.misc[0] = ncons;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kPlanThreads;
+        if (i < NH) sHpre[i] = a.hpre[i] = hv[k];
+        if (i < NS) sSpre[i] = a.spre[i] = sv[k];
+      }
+    }
+    // overflow rows: ranks without moves past their B slots are written by one
+    // thread each; the others (listed in the dead fill records) by a wave each
+    int* sOvr = sScan + 32;
+    for (int r = tid; r < R; r += kPlanThreads) {
+      const int f = sRecv[r];
+      const int m0 = f >= 0 ? sFm0[f] : 0, m1 = f >= 0 ? sFm1[f] : 0;
+      if (m1 - m0 > B) {
+        sOvr[atomicAdd(&sNov, 1)] = r;
+      } else {
+        sOt[r] = 0;
+        a.rinfo[3 * r + 0] = 0;
+        a.rinfo[3 * r + 1] = m0 + B;
+        a.rinfo[3 * r + 2] = m1;
+      }
+    }
+    __syncthreads();
+    for (int q = wave; q < sNov; q += kRouteWaves) {
+      const int r = sOvr[q], f = sRecv[r];
+      const int m0 = sFm0[f], m1 = sFm1[f];
+      int carry = 0;
+      for (int m = m0 + B + lane; m - lane < m1; m += kWave) {     // overflow moves
+        const int len = m < m1 ? sMhi[m] - sMlo[m] : 0;
+        const int incl = wave_incl_scan(len);
+        if (m < m1) sOcum[m] = a.ocum[m] = carry + incl;
+        carry += wave_bcast(incl, kWave - 1);
+      }
+      if (lane == 0) {
+        sOt[r] = carry;
+        a.rinfo[3 * r + 0] = carry;                 // overflow rows
+        a.rinfo[3 * r + 1] = m0 + B;                // overflow moves [m0 + B, m1)
+        a.rinfo[3 * r + 2] = m1;
+      }
+    }
+    __syncthreads();
   }
-  for (int r = wave; r < R; r += kRouteWaves) {
-    const int f = sRecv[r];
-    const int m0 = f >= 0 ? sFm0[f] : 0, m1 = f >= 0 ? sFm1[f] : 0;
-    const int nred = m1 - m0;
-    int carry = 0;
-    for (int t0 = 0; t0 < n; t0 += kWave) {
-      const int t = t0 + lane;
-      const int len = t < n ? sT[r * n + t] - sTaken[r * n + t] : 0;
-      const int incl = wave_incl_scan(len);
-      if (t < n) sHpre[r * (n + 1) + t] = a.hpre[r * (n + 1) + t] = carry + incl - len;
-      carry += wave_bcast(incl, kWave - 1);
-    }
-    if (lane == 0) sHpre[r * (n + 1) + n] = a.hpre[r * (n + 1) + n] = carry;
-    carry = 0;
-    for (int b0 = 0; b0 < B; b0 += kWave) {
-      const int b = b0 + lane;
-      const int len = (b < B && b < nred) ? sMhi[m0 + b] - sMlo[m0 + b] : 0;
-      const int incl = wave_incl_scan(len);
-      if (b < B) sSpre[r * (B + 1) + b] = a.spre[r * (B + 1) + b] = carry + incl - len;
-      carry += wave_bcast(incl, kWave - 1);
-    }
-    if (lane == 0) sSpre[r * (B + 1) + B] = a.spre[r * (B + 1) + B] = carry;
-    carry = 0;
-    for (int m = m0 + B + lane; m - lane < m1; m += kWave) {     // overflow moves
-      const int len = m < m1 ? sMhi[m] - sMlo[m] : 0;
-      const int incl = wave_incl_scan(len);
-      if (m < m1) sOcum[m] = a.ocum[m] = carry + incl;
-      carry += wave_bcast(incl, kWave - 1);
-    }
-    if (lane == 0) {
-      sOt[r] = carry;
-      a.rinfo[3 * r + 0] = carry;                 // overflow rows
-      a.rinfo[3 * r + 1] = m0 + B;                // overflow moves [m0 + B, m1)
-      a.rinfo[3 * r + 2] = m1;
-    }
-  }
-  __syncthreads();
 
   // overflow rows of rank r below weight row j: prefix over its overflow
   // moves (ascending expert) with expert < j
@@ -504,6 +772,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     const int u = sMu[m], f = sRecv[u], b = m - sFm0[f];
     const int row_start = b < B ? cu_at(u, E + b) : cu_at(u, sMe[m]);
     const int pos = sMptr[sMe[m]] + sMpos[m];
+    if ((unsigned)pos >= (unsigned)M) {        // never expected; stay in bounds
+      atomicOr(&sErr, MOE_STATUS_INTERNAL);
+      continue;
+    }
     a.cs_base[pos] = u * SK + row_start - sMlo[m];
     a.cs_lo[pos] = sMlo[m];
     a.cs_hi[pos] = sMhi[m];
