@@ -207,10 +207,12 @@ __device__ __forceinline__ unsigned char* stage_b() {
   else return nullptr;
 }
 
-// Paired row tiles: with MOONEP_GEMM_PAIRA, the data gradient's
-// k-contiguous A operand (dy rows) is loaded two k-tiles at a time, [256 rows][64 k] = 32 KB, so each 16-byte
-// piece of a wave's 1 KB load is part of a whole 128-byte row line instead
-// of half of one.  Three pair buffers (96 KB) plus the four B stages
+// Paired row tiles: with MOONEP_GEMM_PAIRA, the k-contiguous A operand of
+// the forward (xperm rows) and of the data gradient (dy rows) is loaded two
+// k-tiles at a time, [256 rows][64 k] = 32 KB, so each 16-byte piece of a
+// wave's 1 KB load is part of a whole 128-byte row line instead of half of
+// one: the same bytes in half the L2 requests, and a CU keeps only about 64
+// of those in flight.  Three pair buffers (96 KB) plus the four B stages
 // (64 KB) fill the 160 KB of LDS.
 #ifndef MOONEP_GEMM_PAIRA
 #define MOONEP_GEMM_PAIRA 1
@@ -295,9 +297,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   // Operand tiles: a "row tile" holds k-contiguous rows (forward A, and
   // both operands of the data gradient), a "col tile" k-strided rows.
   constexpr bool kRowA = MODE != MODE_WGRAD, kRowB = MODE == MODE_DGRAD;
-  // Paired A tiles pay off where both operands are row tiles (the data
-  // gradient: +5 %); the forward measured the same either way.
-  constexpr bool kPair = MODE == MODE_DGRAD && MOONEP_GEMM_PAIRA && BK == 32 && kNST == 4;
+  // Paired A tiles (the SwiGLU projection keeps single ones: its epilogue
+  // needs the stage arrays beside the pair buffers).
+  constexpr bool kPair = (MODE == MODE_FWD || MODE == MODE_DGRAD) && MOONEP_GEMM_PAIRA &&
+                         BK == 32 && kNST == 4;
   constexpr bool kSwi = MODE == MODE_SWIGLU;
   constexpr bool kNMajor =
       MODE == MODE_DGRAD || ((MODE == MODE_FWD || kSwi) && MOONEP_FWD_NMAJOR);
