@@ -45,7 +45,13 @@ def test_tiny_many_seeds():
     dict(B=0, mode=1), dict(B=1, mode=1), dict(R=64, E=128, S=5, K=3, B=2),
     dict(R=3, E=9, S=7, K=3, B=3), dict(R=16, E=64, S=33, K=7, B=4),
     dict(E=512, R=4, S=40, K=16, B=128), dict(E=2048, R=8, S=20, K=64, B=256),
-    dict(R=1024, E=1024, S=2, K=2, B=1), dict(R=5, E=1000, S=77, K=9, B=200)])
+    dict(R=1024, E=1024, S=2, K=2, B=1), dict(R=5, E=1000, S=77, K=9, B=200),
+    # ranks held 4 per lane in the fill loop; row prefixes as block-wide scans
+    dict(R=128, E=256, S=9, K=4, B=2), dict(R=200, E=400, S=6, K=5, B=2),
+    # inference past the 32-rank threshold: ranks with overflow moves (B = 0:
+    # every move overflows) take the wave-per-rank overflow prefix
+    dict(R=48, E=96, S=11, K=3, B=0, mode=1), dict(R=40, E=160, S=13, K=6, B=1, mode=1),
+    dict(R=300, E=600, S=4, K=3, B=1, mode=1)])
 def test_edge_shapes(kw):
     shape = W.TINY.with_(**kw)
     for seed in range(6):
@@ -145,7 +151,9 @@ def test_largest_policy_tiny_and_edges():
         plan, _ = check_policy(W.TINY, ids, mx.PLAN_LARGEST_FIRST, plan)
     for kw in (dict(R=1, B=8), dict(B=1, mode=1), dict(B=0, mode=1), dict(R=64, E=128, S=5, K=3, B=2),
                dict(E=512, R=4, S=40, K=16, B=128), dict(E=2048, R=8, S=20, K=64, B=256),
-               dict(R=1024, E=1024, S=2, K=2, B=1), dict(R=5, E=1000, S=77, K=9, B=200)):
+               dict(R=1024, E=1024, S=2, K=2, B=1), dict(R=5, E=1000, S=77, K=9, B=200),
+               dict(R=128, E=256, S=9, K=4, B=2), dict(R=48, E=96, S=11, K=3, B=0, mode=1),
+               dict(R=300, E=600, S=4, K=3, B=1, mode=1)):
         shape = W.TINY.with_(**kw)
         for seed in range(4):
             if seed == 3:
