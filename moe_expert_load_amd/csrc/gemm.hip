@@ -40,7 +40,10 @@
 // gradient) is stored as loaded, [k][col], and read with the transposing
 // ds_read_b64_tr_b16, which returns 4 consecutive k per lane.  Fragment
 // reads of the next 16-deep substep are interleaved with the MFMAs of the
-// current one.
+// current one.  The A operand of the forward and of the data gradient (a row
+// tile) goes in pairs of k-tiles through three 32 KB buffers, so its loads
+// are whole 128-byte lines: a CU keeps only about 64 L2 requests in flight,
+// and that bound, not the matrix pipe, sets these kernels' speed.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
