@@ -1209,8 +1209,8 @@ static size_t gemm_ws_bytes(const moe_cfg* c) {
 // moe_expert_load_amd/calibrate.py to forward and data-gradient GEMM times
 // on one MI355X (the SwiGLU projection uses the forward's).
 struct CostModel { int32_t tile, k, k_block, launch; };
-constexpr CostModel kCostFwd = {6119789, 554595, 122365, 0};
-constexpr CostModel kCostDgrad = {6399523, 680492, 83723, 42240708};
+constexpr CostModel kCostFwd = {7118903, 522523, 125859, 0};
+constexpr CostModel kCostDgrad = {5988999, 682007, 87206, 47041760};
 
 // Average rows per home segment, S*K*R/E, below which a step's tails are a
 // large enough share of its tiles for the class-2 and class-1 launches to
