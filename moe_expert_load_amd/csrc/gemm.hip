@@ -303,10 +303,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   // Operand tiles: a "row tile" holds k-contiguous rows (forward A, and
   // both operands of the data gradient), a "col tile" k-strided rows.
   constexpr bool kRowA = MODE != MODE_WGRAD, kRowB = MODE == MODE_DGRAD;
-  // Paired A tiles (the SwiGLU projection keeps single ones: its epilogue
-  // needs the stage arrays beside the pair buffers).
-  constexpr bool kPair = (MODE == MODE_FWD || MODE == MODE_DGRAD) && MOONEP_GEMM_PAIRA &&
-                         BK == 32 && kNST == 4;
+  // Paired A tiles wherever A is a row tile (forward, data gradient, SwiGLU
+  // projection).
+  constexpr bool kPair = (MODE == MODE_FWD || MODE == MODE_DGRAD || MODE == MODE_SWIGLU) &&
+                         MOONEP_GEMM_PAIRA && BK == 32 && kNST == 4;
   constexpr bool kSwi = MODE == MODE_SWIGLU;
   constexpr bool kNMajor =
       MODE == MODE_DGRAD || ((MODE == MODE_FWD || kSwi) && MOONEP_FWD_NMAJOR);
@@ -810,7 +810,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // row piece goes out as one 16-byte store: act to act[:, a], gate to
       // h13[:, a], up to h13[:, H' + a].  sigmoid uses the hardware
       // reciprocal (1 ulp), far inside the bf16 rounding of the output.
-      unsigned char* Ca = epilogue_area(wv);
+      // with paired A tiles the stage arrays of A do not exist: the wave's
+      // first area is its 16 KB of the pair buffers, as in the forward
+      unsigned char* Ca = kPair ? (wv < 2 ? g_pa0 : g_pa1) + (wv & 1) * 16384 : epilogue_area(wv);
       unsigned char* Cg = epilogue_area2(wv);
       const int a0 = tn * (BN / 2) + wn * 64;
       const bool keep = g.h13 != nullptr;
