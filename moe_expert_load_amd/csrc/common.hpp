@@ -105,16 +105,5 @@ __device__ __forceinline__ int wave_max(int v) {
   return wave_bcast(v, kWave - 1);
 }
 
-// Lanes of the wave whose key equals this lane's key, restricted to `active`.
-// One ballot per key bit: a lane matches iff it agrees on every bit.
-__device__ __forceinline__ uint64_t match_any(int key, int nbits, uint64_t active) {
-  uint64_t m = active;
-  for (int b = 0; b < nbits; ++b) {
-    const int bit = (key >> b) & 1;
-    const uint64_t bal = __ballot(bit);
-    m &= bit ? bal : ~bal;
-  }
-  return m;
-}
 
 }  // namespace moonep

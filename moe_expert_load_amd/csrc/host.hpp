@@ -48,7 +48,6 @@ struct PlanLayout {
   int L;          // slots per wave sub-chunk (multiple of 64)
   int C;          // chunks of 16 sub-chunks (one workgroup each)
   int M;          // move capacity E + R - 1
-  int nbits;      // bits needed for keys in [0, E]
   size_t off_cc, off_badc, off_taken, off_home_base, off_mptr, off_mcnt, off_cs_lo, off_cs_hi,
       off_cs_base, off_cs_dst, off_cs_b, off_cons, off_hpre, off_spre, off_rinfo, off_ocum,
       off_misc, bytes;
@@ -69,9 +68,6 @@ inline PlanLayout plan_layout(const moe_cfg* c) {
   const int64_t ch = int64_t(kRouteWaves) * p.L;
   p.C = (int)((p.N + ch - 1) / ch);
   p.M = c->E + c->R - 1;
-  int nb = 0;
-  while ((1 << nb) <= c->E) ++nb;
-  p.nbits = nb;
   size_t o = 0;
   auto take = [&](size_t ints) { size_t at = o; o += align256(ints * 4); return at; };
   p.off_cc = take(size_t(p.C > 0 ? p.C : 1) * c->E);

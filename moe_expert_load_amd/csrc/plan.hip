@@ -28,7 +28,7 @@ struct IntTag {
 
 struct PlanArgs {
   const int32_t* ids;
-  int32_t N, R, S, E, K, B, mode, n, SK, L, C, M, nbits, policy;
+  int32_t N, R, S, E, K, B, mode, n, SK, L, C, M, policy;
   int32_t *counts, *load0, *route, *cu, *slot_expert, *n_red, *src_rank, *moves, *status;
   int32_t *cc, *badc, *taken, *home_base, *mptr, *mcnt, *cs_lo, *cs_hi, *cs_base, *cs_dst, *cs_b,
       *cons, *hpre, *spre, *rinfo, *ocum, *misc;
@@ -968,17 +968,32 @@ __global__ __launch_bounds__(kPlanThreads) void k_route(PlanArgs a) {
     }
   }
   __syncthreads();
-  // pass B: ranks and destinations
+  // pass B: ranks and destinations.  Each slot takes a provisional rank
+  // from one LDS fetch-add on its expert's counter (lanes of a round that
+  // share an expert get consecutive values, in an order the hardware
+  // picks); the lanes of every key that more than one lane holds are then
+  // ranked again in lane order, one ballot per such key.  The counter ends
+  // each round advanced by the round's slots of that expert either way.
   auto route8 = [&](int64_t b0, const int* ids8) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t i = b0 + u * kWave + lane;
       const int key = ids8[u];
-      const uint64_t act = __ballot(key < E);
-      if (act == 0) continue;
-      const uint64_t m = match_any(key, a.nbits, act);
-      if (key < E) {
-        const int p = cnt[key] + (int)__popcll(m & lt);
+      const bool ok = key < E;
+      int before = 0, p = 0;
+      if (ok) {
+        before = cnt[key];
+        p = atomicAdd(&cnt[key], 1);
+      }
+      uint64_t pend = __ballot(ok && p != before);     // lanes not served first
+      while (pend) {
+        const int ld = __ffsll((unsigned long long)pend) - 1;
+        const int k = wave_bcast(key, ld);
+        const uint64_t m = __ballot(ok && key == k);
+        if (ok && key == k) p = before + (int)__popcll(m & lt);
+        pend &= ~m;
+      }
+      if (ok) {
         int dest = -1;
         if (p >= s_taken[key]) {
           dest = s_home[key] + p;
@@ -993,13 +1008,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_route(PlanArgs a) {
         }
         a.route[i] = dest;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (key < E && (m & lt) == 0) cnt[key] += (int)__popcll(m);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   };
   route8(base, first);
@@ -1054,7 +1062,7 @@ extern "C" int moe_plan_run_policy(const moe_cfg* cfg, const int32_t* topk_ids,
   a.R = cfg->R; a.S = cfg->S; a.E = cfg->E; a.K = cfg->K; a.B = cfg->B; a.mode = cfg->mode;
   a.n = cfg->E / cfg->R;
   a.SK = cfg->S * cfg->K;
-  a.L = L.L; a.C = L.C; a.M = L.M; a.nbits = L.nbits;
+  a.L = L.L; a.C = L.C; a.M = L.M;
   a.policy = policy;
   a.counts = plan->counts; a.load0 = plan->load0; a.route = plan->route; a.cu = plan->cu_seqlens;
   a.slot_expert = plan->slot_expert; a.n_red = plan->n_redundant; a.src_rank = plan->src_rank;
