@@ -75,6 +75,7 @@ def log(*a):
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_bench_shape.txt")
 KERNEL_SOURCES = {"k_gemm<0>": "moe_expert_load_amd/csrc/gemm.hip",
+                  "k_wgrad": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<1>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<2>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<3>": "moe_expert_load_amd/csrc/gemm.hip",
@@ -1269,7 +1270,7 @@ def main():
                          "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "ms": ms[name]})
             comps[name + "_GBps"] = ach
     comps["plan_us"] = ms["plan"] * 1e3
-    step_kernel = {"gemm": "k_gemm<0>", "wgrad": "k_gemm<1>", "dispatch": "k_dispatch",
+    step_kernel = {"gemm": "k_gemm<0>", "wgrad": "k_wgrad", "dispatch": "k_dispatch",
                    "combine": "k_combine", "prefetch": "k_prefetch",
                    "reduce_grad": "k_reduce_grad", "plan": None}
     for r in roof:
@@ -1277,11 +1278,11 @@ def main():
         r["traffic"] = measured_traffic(k) if k else None
     dom = max((r for r in roof if r["step"] != "plan"), key=lambda r: r["ms"])
     kernel_of = {"gemm": "k_gemm<0> (grouped GEMM, 256x256 MFMA tiles)",
-                 "wgrad": "k_gemm<1> (weight-grad GEMM)",
+                 "wgrad": "k_wgrad (weight-grad GEMM, 384x256 MFMA tiles)",
                  "dispatch": "k_dispatch", "combine": "k_combine",
                  "prefetch": "k_prefetch", "reduce_grad": "k_reduce_grad"}
     gemm_units = units[dom["step"]][1]
-    dom_kernel = {"gemm": "k_gemm<0>", "wgrad": "k_gemm<1>", "dispatch": "k_dispatch",
+    dom_kernel = {"gemm": "k_gemm<0>", "wgrad": "k_wgrad", "dispatch": "k_dispatch",
                   "combine": "k_combine", "prefetch": "k_prefetch",
                   "reduce_grad": "k_reduce_grad"}[dom["step"]]
     roofline = {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],

@@ -295,8 +295,9 @@ int moe_combine(const moe_cfg *cfg, const moe_plan *plan, const moe_bf16 *y,
  *                    expert; other slots are not written.
  * xperm [R][S*K][H] bf16, dy [R][S*K][Hp] bf16, grad_home [E][H][Hp],
  * grad_pref [R][B][H][Hp].  `workspace` as for moe_grouped_gemm.
- * Hp must stay below 2^21 (a 256-row tile of one gradient then spans less
- * than 2 GiB, the reach of the stores' 32-bit offsets), else MOE_ELIMIT.
+ * Hp must stay at or below 1398101 (a 384-row tile of one gradient then
+ * spans less than 2 GiB, the reach of the stores' 32-bit offsets), else
+ * MOE_ELIMIT.
  */
 int moe_grouped_gemm_wgrad(const moe_cfg *cfg, const moe_plan *plan,
                            const moe_bf16 *xperm, const moe_bf16 *dy,

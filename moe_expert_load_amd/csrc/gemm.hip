@@ -20,8 +20,10 @@
 //               CUs of one XCD share each weight panel across the band's row
 //               tiles in that XCD's L2, and a long segment streams its rows
 //               once per band rather than once per column tile.
-//   MODE 0: y = xperm_seg @ W (forward); MODE 1: G = xperm_seg^T @ dy_seg
-//   (weight gradient, fp32); MODE 2: dxperm_seg = dy_seg @ W^T (data
+//   k_wgrad     the weight gradient G = xperm_seg^T @ dy_seg (fp32) on
+//               384 x 256 tiles with 8 waves (see its own comment).
+//   MODE 0: y = xperm_seg @ W (forward); MODE 1: the weight gradient on
+//   256 x 256 tiles (built with MOONEP_WGRAD_WIDE=0); MODE 2: dxperm_seg = dy_seg @ W^T (data
 //   gradient, over the forward's work list); MODE 3: the first projection
 //   of a SwiGLU expert, act = silu(x W_gate) * (x W_up) with W13 = [W_gate |
 //   W_up] in one [E+B, H, 2H'] tensor -- each 256-column tile takes 128
@@ -74,6 +76,17 @@ constexpr int kGemmThreads = 256;
 // share its x^T and dy panels in that XCD's L2.
 #ifndef MOONEP_WGRAD_XCD
 #define MOONEP_WGRAD_XCD 1
+#endif
+
+// Weight gradient: the next tile's first k-tiles are loaded during the
+// current tile's store burst (1), or after it (0).
+#ifndef MOONEP_WGRAD_CARRY
+#define MOONEP_WGRAD_CARRY 1
+#endif
+
+// Weight gradient: 384 x 256 tiles (k_wgrad, 1) or 256 x 256 (k_gemm, 0).
+#ifndef MOONEP_WGRAD_WIDE
+#define MOONEP_WGRAD_WIDE 1
 #endif
 
 // Row-tile A operands interleave the two wave rows by 32-row blocks: wave
@@ -376,9 +389,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   // (declared once here, the data gradient measured 2 % faster than with a
   // fresh array per tile).
   f32x16 acc[4][4];
-  for (int64_t q = 0;; ++q) {
-    const int64_t w = kXcdItems ? wbeg + q * per + local : q * G + int64_t(xcd) * per + local;
-    if (w >= wend) break;
+  // Work index of this workgroup's q-th tile.
+  auto work_index = [&](int64_t q) -> int64_t {
+    return kXcdItems ? wbeg + q * per + local : q * G + int64_t(xcd) * per + local;
+  };
+  const int arow = MODE == MODE_DGRAD ? Hp : H;          // A row length
+  // Everything a tile's loads need: its place, its k-tile count, the two
+  // range-checked operand resources and this lane's offsets into them.
+  struct Tile {
+    WorkItem it;
+    int tm, tn, KD, nk;
+    u32x4 ra, rb;
+    uint32_t goa[NI], gob[NI];
+  };
+  auto setup = [&](int64_t w) -> Tile {
     int tm, tn;
     WorkItem it;
     if (kNMajor) {
@@ -406,9 +430,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     }
     const int n0 = tn * BN, m0 = tm * BM;
     const int KD = (MODE == MODE_FWD || kSwi) ? H : MODE == MODE_DGRAD ? Hp : it.rows;
-    // k-tiles, rounded up to whole passes over the stages: tiles past the
-    // end load zeros (range-checked loads; ragged forward K is zeroed below)
-    const int nk = ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
+    // k-tiles: the weight gradient's K is the segment's row count, so it
+    // runs exactly the k-tiles that hold rows (the last one ragged: its rows
+    // past the segment load zeros); the fixed-K modes round up to whole
+    // passes over the stages (tiles past the end load zeros; ragged forward
+    // K is zeroed below)
+    const int nk = MODE == MODE_WGRAD ? (KD + BK - 1) / BK
+                                      : ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
 
     // Operand A: forward = xperm rows of the segment (row tile); weight
     // gradient = the same rows read as x^T (col tile over h); data gradient
@@ -416,7 +444,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     // Operand B: forward = weight W(r, j) [H][Hp] (col tile); weight
     // gradient = dy rows (col tile); data gradient = W(r, j) read as W^T,
     // i.e. rows h of W with k = h' contiguous (row tile).
-    const int arow = MODE == MODE_DGRAD ? Hp : H;        // A row length
     const uint16_t* Abase = (MODE == MODE_DGRAD ? g.dy : g.xperm) + int64_t(it.row0) * arow;
     const uint16_t* Bbase;
     uint32_t bbytes;
@@ -428,11 +455,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       Bbase = g.dy + int64_t(it.row0) * Hp;
       bbytes = uint32_t(it.rows) * Hp * 2;
     }
-    const u32x4 ra = make_rsrc(Abase, uint32_t(it.rows) * arow * 2);
-    const u32x4 rb = make_rsrc(Bbase, bbytes);
+    Tile X;
+    X.it = it;
+    X.tm = tm;
+    X.tn = tn;
+    X.KD = KD;
+    X.nk = nk;
+    X.ra = make_rsrc(Abase, uint32_t(it.rows) * arow * 2);
+    X.rb = make_rsrc(Bbase, bbytes);
 
     // Per-lane global byte offsets of this wave's load instructions.
-    uint32_t goa[NI], gob[NI];
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
       const int t = wv * NI + u;
@@ -442,15 +474,62 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // col tile: load t covers k rows 2t, 2t+1 of 256 columns
       const int crow = t * 2 + (lane >> 5);
       const int cc = (lane & 31) ^ (4 * (crow & 3));
-      if (kRowA) goa[u] = uint32_t(rrow) * arow * 2 + rkc * 16;
-      else goa[u] = uint32_t(crow) * H * 2 + uint32_t(m0 + 8 * cc) * 2;
+      if (kRowA) X.goa[u] = uint32_t(rrow) * arow * 2 + rkc * 16;
+      else X.goa[u] = uint32_t(crow) * H * 2 + uint32_t(m0 + 8 * cc) * 2;
       // SwiGLU: 32-column block b of the tile is gate (b even) or up (b odd)
       // of activation columns tn*128 + (b/2)*32 + [0, 32).  Columns past the
       // activation width only feed accumulators that are never stored.
       const int col = kSwi ? ((cc >> 2) & 1) * Hp + tn * (BN / 2) + (cc >> 3) * 32 + 8 * (cc & 3)
                            : n0 + 8 * cc;
-      if (kRowB) gob[u] = uint32_t(n0 + rrow) * Hp * 2 + rkc * 16;
-      else gob[u] = uint32_t(crow) * WC * 2 + uint32_t(col) * 2;
+      if (kRowB) X.gob[u] = uint32_t(n0 + rrow) * Hp * 2 + rkc * 16;
+      else X.gob[u] = uint32_t(crow) * WC * 2 + uint32_t(col) * 2;
+    }
+    return X;
+  };
+  // Direct loads of k-tile kt of tile X into stage S (= kt % kNST).
+  auto issue_tile = [&](const Tile& X, auto S_, int kt) {
+    constexpr int S = decltype(S_)::value;
+    unsigned char* As = stage_a<S>();
+    unsigned char* Bs = stage_b<S>();
+    const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+    const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      load_lds16(X.ra, As + (wv * NI + u) * 1024, X.goa[u], ka);
+      load_lds16(X.rb, Bs + (wv * NI + u) * 1024, X.gob[u], kb);
+    }
+  };
+  // The first min(nk, kNST) k-tiles of tile X, one per stage.
+  auto issue_first = [&](const Tile& X) {
+    issue_tile(X, std::integral_constant<int, 0>(), 0);
+    if (X.nk > 1) issue_tile(X, std::integral_constant<int, 1>(), 1);
+    if constexpr (kNST >= 4) {
+      if (X.nk > 2) issue_tile(X, std::integral_constant<int, 2 % kNST>(), 2);
+      if (X.nk > 3) issue_tile(X, std::integral_constant<int, 3 % kNST>(), 3);
+    }
+    if constexpr (kNST == 5)
+      if (X.nk > 4) issue_tile(X, std::integral_constant<int, 4 % kNST>(), 4);
+  };
+  // Weight gradient: before a tile's stores go out, the next tile's first
+  // stages are issued, so its loads run during the store burst instead of
+  // after it (the stage arrays are free once the k-loop has ended).
+  constexpr bool kCarry = MODE == MODE_WGRAD && MOONEP_WGRAD_CARRY;
+  Tile nxt;
+  bool have_nxt = false;
+  for (int64_t q = 0;; ++q) {
+    const int64_t w = work_index(q);
+    if (w >= wend) break;
+    const bool carried = kCarry && have_nxt;
+    const Tile T = carried ? nxt : setup(w);
+    const WorkItem it = T.it;
+    const int tm = T.tm, tn = T.tn, KD = T.KD, nk = T.nk;
+    const int n0 = tn * BN, m0 = tm * BM;
+    const u32x4 ra = T.ra, rb = T.rb;
+    uint32_t goa[NI], gob[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      goa[u] = T.goa[u];
+      gob[u] = T.gob[u];
     }
 
     // paired A loads: load t (8 per wave) covers rows 8t .. 8t+7, whole lines
@@ -609,7 +688,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // At publish(kt) the loads of k-tiles kt+1 .. kt+kNST-2 may stay in flight.
       auto publish = [&](int kt) {
         const int after = min(kNST - 2, nk - 1 - kt);
-        if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
+        // a carried tile's first pass has landed already (see below)
+        if (carried && kt < kNST) {
+        } else if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
         else if (kNST >= 4 && after >= 2) wait_vm<4 * NI>();
         else if (kNST >= 3 && after == 1) wait_vm<2 * NI>();
         else wait_vm<0>();
@@ -771,33 +852,60 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
           step_pair(std::integral_constant<int, 2>(), kt + 2);
           step_pair(std::integral_constant<int, 3>(), kt + 3);
         }
-      } else if (nk > 0) {                                        // then nk >= kNST
-      issue(std::integral_constant<int, 0>(), 0);
-      issue(std::integral_constant<int, 1>(), 1);
-      if constexpr (kNST >= 4) {
-        issue(std::integral_constant<int, 2 % kNST>(), 2);
-        issue(std::integral_constant<int, 3 % kNST>(), 3);
+      } else if (nk > 0) {
+      // k-tile 0 has landed once the later k-tiles of the first pass (2 NI
+      // loads each) are all that is left in flight.  A carried tile's first
+      // pass went out before the previous tile's stores: a full tile's 256
+      // store instructions per wave follow it (more than the 63 a wave keeps
+      // in flight, and completions count in issue order), and after a
+      // partial tile's stores the wave waited for everything -- so at most
+      // 62 pending operations leave the whole first pass landed.
+      if (carried) {
+        wait_vm<62>();
+      } else {
+        issue_first(T);
+        const int later = min(nk, kNST) - 1;
+        if constexpr (kNST >= 5) {
+          if (later >= 4) wait_vm<4 * 2 * NI>();
+        }
+        if (later == 3) wait_vm<3 * 2 * NI>();
+        else if (later == 2) wait_vm<2 * 2 * NI>();
+        else if (later == 1) wait_vm<2 * NI>();
+        else if (later == 0) wait_vm<0>();
       }
-      if constexpr (kNST == 5) issue(std::integral_constant<int, 4 % kNST>(), 4);
-      // k-tile 0 has landed once the kNST - 1 later k-tiles (2 NI loads each)
-      // are all that is left in flight
-      wait_vm<(kNST - 1) * 2 * NI>();
       barrier_lds();
       read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
+      // nk need not be a multiple of kNST (weight gradient): stop after its
+      // last k-tile
       for (int kt = 0; kt < nk; kt += kNST) {
         step(std::integral_constant<int, 0>(), kt);
+        if (kt + 1 >= nk) break;
         step(std::integral_constant<int, 1>(), kt + 1);
         if constexpr (kNST >= 4) {
+          if (kt + 2 >= nk) break;
           step(std::integral_constant<int, 2 % kNST>(), kt + 2);
+          if (kt + 3 >= nk) break;
           step(std::integral_constant<int, 3 % kNST>(), kt + 3);
         }
-        if constexpr (kNST == 5) step(std::integral_constant<int, 4 % kNST>(), kt + 4);
+        if constexpr (kNST == 5) {
+          if (kt + 4 >= nk) break;
+          step(std::integral_constant<int, 4 % kNST>(), kt + 4);
+        }
       }
       }
     };
     pipeline(std::integral_constant<int, NBK>());
     wait_vm<0>();
     __syncthreads();
+    // every wave is done with the stage arrays: start the next tile's loads
+    if constexpr (kCarry) {
+      const int64_t wn = work_index(q + 1);
+      have_nxt = wn < wend;
+      if (have_nxt) {
+        nxt = setup(wn);
+        if (nxt.nk > 0) issue_first(nxt);
+      }
+    }
 
     // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
     // rows 8*(v/4) + 4*(l/32) + v%4 of its block for v = 0..15.
@@ -916,7 +1024,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // 32-63, four rows apart).  Full tiles skip the bounds checks.  Buffer
       // stores (non-temporal) over this tile's rows: 32-bit offsets from one
       // descriptor instead of a 64-bit address per store (1.3 % faster); the
-      // entry point keeps a tile's rows under 2 GiB (H' < 2^21).
+      // entry point keeps a tile's rows under 2 GiB (384 H' 4 < 2^31).
       float* out = it.j < g.E ? g.grad_home + int64_t(it.j) * H * Hp
                               : g.grad_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
       const int trows = min(BM, H - m0);
@@ -941,9 +1049,278 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
             }
           }
       };
-      if (m0 + BM <= H && n0 + BN <= Hp) store_tile(std::true_type());
-      else store_tile(std::false_type());
+      if (m0 + BM <= H && n0 + BN <= Hp) {
+        store_tile(std::true_type());
+      } else {
+        store_tile(std::false_type());
+        // a partial tile's stores may be fewer than the carried loads' wait
+        // assumes (see the pipeline): wait for everything
+        if (kCarry && have_nxt) wait_vm<0>();
+      }
       __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradient on 384 x 256 tiles (384 rows of G over h, 256 columns over
+// h').  Like the other GEMMs, this kernel is bound by how fast one CU pulls
+// operand lines through its L1 (a CU keeps about 64 requests in flight), not
+// by the matrix pipe, so what counts is operand bytes per multiply-add: a
+// 384 x 256 tile needs (384 + 256) / (384 * 256) of them per k, a sixth less
+// than a 256 x 256 tile.  Its 384 KB of fp32 accumulators take 8 waves (2 per
+// SIMD), each with 3 x 4 MFMA blocks of 32 x 32 (192 AGPRs) and at most 64
+// other registers, so the layout is chosen to need few per-lane offsets:
+//  * wave (wm, wn) = (wave % 4, wave / 4) takes the tile's 32-row blocks
+//    wm + 4i (i < 3) and 32-column blocks wn + 2j (j < 4);
+//  * a stage holds x^T as three [32 k][128 h] sub-tiles (256-byte rows) and
+//    dy as one [32 k][256 h'] tile (512-byte rows), both stored as loaded
+//    ("col tiles", k strided) with 16-byte chunk c of row k at c ^ 4 (k % 4),
+//    and read with the transposing LDS read (see lds_tr), conflict free;
+//  * every x^T load instruction fills 4 rows x 256 bytes of a sub-tile and
+//    every dy load 2 rows x 512 bytes (whole 128-byte lines), so a lane's
+//    global offset is one of three values plus a wave-uniform part.
+// A wave keeps one set of fragments: the other wave on its SIMD runs its
+// MFMAs while it waits for the next.  Four 40 KB stages fill the 160 KB of
+// LDS.  The next tile's first pass is issued before the current tile's
+// stores, as in k_gemm's weight gradient.
+// ---------------------------------------------------------------------------
+constexpr int WBM = 384;                 // h rows per tile
+constexpr int kWThreads = 512;           // 8 waves
+constexpr int kWSub = 32 * 128 * 2;      // one x^T sub-tile (8 KB)
+constexpr int kWA = 3 * kWSub;           // x^T stage (24 KB)
+constexpr int kWB = 32 * BN * 2;         // dy stage (16 KB)
+constexpr int kWStage = kWA + kWB;       // one stage: x^T then dy (40 KB)
+constexpr int kWNA = kWA / 1024 / 8;     // x^T loads per wave per k-tile (3)
+constexpr int kWNB = kWB / 1024 / 8;     // dy loads per wave per k-tile (2)
+constexpr int kWL = kWNA + kWNB;         // loads per wave per k-tile (5)
+static_assert(kWNA == 3 && kWNB == 2 && 3 * kWL < 63, "weight-gradient tile");
+__shared__ __attribute__((aligned(1024))) unsigned char g_wst[4 * kWStage];
+
+__global__ __launch_bounds__(kWThreads, 1) void k_wgrad(GemmArgs g) {
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wv & 3, wn = wv >> 2;
+  const int H = g.H, Hp = g.Hp;
+  const int ntm = (H + WBM - 1) / WBM, ntn = (Hp + BN - 1) / BN;
+  const int per = gridDim.x / 8;
+  const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  // XCD x owns the tiles of items [nitems[8+x], nitems[9+x]) (contiguous,
+  // balanced by predicted time), so a segment's tiles share its x^T and dy
+  // panels in that XCD's L2
+  const int64_t wbeg = int64_t(g.nitems[8 + xcd]) * ntm * ntn;
+  const int64_t wend = int64_t(g.nitems[9 + xcd]) * ntm * ntn;
+
+  // Transposing fragment reads: lane group G4 = lane/16 takes k half G4/2
+  // and column half G4%2 of a 32-column block; row k = tr_k (+4, +16 s) has
+  // k % 4 = li / 4.  Block 4q + b of a 16-chunk row group sits at chunks
+  // (4b + cl) ^ sw.  This wave's x^T blocks wm + 4i all have b = wm (sub-tile
+  // i); its dy blocks wn + 2j have b = wn or wn + 2 (row group j / 2).
+  const int G4 = lane >> 4, li = lane & 15;
+  const int tr_k = 8 * (G4 >> 1) + (li >> 2);
+  const int cl = 2 * (G4 & 1) + ((li & 3) >> 1), sw = 4 * (li >> 2);
+  int pa = tr_k * 256 + (((4 * wm + cl) ^ sw) << 4) + 8 * (li & 1);
+  int pb[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    pb[e] = tr_k * 512 + (((4 * (2 * e + wn) + cl) ^ sw) << 4) + 8 * (li & 1);
+  // Direct loads.  x^T load t (0..23 per stage) fills rows 4 (t % 8) + [0, 4)
+  // of sub-tile t / 8: lane l takes row + l / 16 and stored chunk l % 16.
+  // dy load t (0..15) fills rows 2t, 2t + 1: lane l takes row 2t + l / 32 and
+  // stored chunk l % 32, whose logical chunk depends on t % 2.
+  const uint32_t la = uint32_t(lane >> 4) * H * 2 + (((lane & 15) ^ (4 * (lane >> 4))) << 4);
+  uint32_t lb[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    lb[e] = uint32_t(lane >> 5) * Hp * 2 + (((lane & 31) ^ (4 * ((2 * e + (lane >> 5)) & 3))) << 4);
+
+  typedef __attribute__((address_space(4))) const WorkItem const_item;
+  const const_item* items = (const const_item*)g.items;
+  struct Tile {
+    int r, j, tm, tn, nk;
+    u32x4 ra, rb;
+  };
+  auto setup = [&](int64_t w) -> Tile {
+    const int64_t item = w / (ntm * ntn);
+    const int rest = (int)(w % (ntm * ntn));
+    Tile t;
+    t.r = items[item].r;
+    t.j = items[item].j;
+    const int row0 = items[item].row0, rows = items[item].rows;
+    t.tm = rest / ntn;
+    t.tn = rest % ntn;
+    t.nk = (rows + 31) / 32;              // the last k-tile's rows past the segment read zeros
+    t.ra = make_rsrc(g.xperm + int64_t(row0) * H, uint32_t(rows) * H * 2);
+    t.rb = make_rsrc(g.dy + int64_t(row0) * Hp, uint32_t(rows) * Hp * 2);
+    return t;
+  };
+  // Loads of k-tile kt of tile X into its stage kt % 4 (this wave's pieces).
+  auto issue = [&](const Tile& X, int kt) {
+    unsigned char* st = g_wst + (kt & 3) * kWStage;
+    const uint32_t ka = uint32_t(kt) * 32 * H * 2 + uint32_t(X.tm) * WBM * 2;
+    const uint32_t kb = uint32_t(kt) * 32 * Hp * 2 + uint32_t(X.tn) * BN * 2;
+#pragma unroll
+    for (int u = 0; u < kWNA; ++u) {
+      const int t = wv * kWNA + u;
+      load_lds16(X.ra, st + t * 1024, la, ka + uint32_t(4 * (t & 7)) * H * 2 + (t >> 3) * 256);
+    }
+#pragma unroll
+    for (int u = 0; u < kWNB; ++u) {
+      const int t = wv * kWNB + u;
+      load_lds16(X.rb, st + kWA + t * 1024, lb[u], kb + uint32_t(2 * t) * Hp * 2);
+    }
+  };
+  // the first min(nk, 4) k-tiles of X, one per stage
+  auto issue_first = [&](const Tile& X) {
+    for (int kt = 0; kt < min(X.nk, 4); ++kt) issue(X, kt);
+  };
+
+  f32x16 acc[3][4];
+  bf16x8 fa[3], fb[4];
+  Tile nxt;
+  bool have_nxt = false;
+  for (int64_t w = wbeg + local; w < wend; w += per) {
+    const bool carried = have_nxt;
+    const Tile T = carried ? nxt : setup(w);
+    const int nk = T.nk;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // fragments of 16-deep substep s of the stage at st (its x^T sub-tile i,
+    // its dy row group j / 2); qa, qb: this lane's offsets into the stage
+    auto read_a = [&](int qa, int s, int i) {
+      const unsigned char* p = g_wst + qa + s * 16 * 256 + i * kWSub;
+      fa[i] = join(lds_tr(p), lds_tr(p + 4 * 256));
+    };
+    auto read_b = [&](const int (&qb)[2], int s, int j) {
+      const unsigned char* p = g_wst + qb[j & 1] + kWA + s * 16 * 512 + (j >> 1) * 256;
+      fb[j] = join(lds_tr(p), lds_tr(p + 4 * 512));
+    };
+    auto mfma_row = [&](int i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+
+    if (nk > 0) {
+      // k-tile 0 has landed once the later k-tiles of the first pass are
+      // all that is left in flight.  A carried tile's first pass went out
+      // before the previous tile's stores: a full tile's 192 store
+      // instructions per wave follow it (more than the 63 a wave keeps in
+      // flight, and completions count in issue order), and after a partial
+      // tile's stores the wave waited for everything -- so at most 62
+      // pending operations leave the whole first pass landed.
+      if (carried) {
+        wait_vm<62>();
+      } else {
+        issue_first(T);
+        const int later = min(nk, 4) - 1;
+        if (later == 3) wait_vm<3 * kWL>();
+        else if (later == 2) wait_vm<2 * kWL>();
+        else if (later == 1) wait_vm<kWL>();
+        else wait_vm<0>();
+      }
+      barrier_lds();
+      {
+        int qb[2] = {pb[0], pb[1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) read_b(qb, 0, j);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) read_a(pa, 0, i);
+      }
+      for (int kt = 0; kt < nk; ++kt) {
+        // this lane's offsets into the stage of k-tile kt and of kt + 1,
+        // computed here (a few idle VALU cycles) rather than kept per stage
+        const int so = (kt & 3) * kWStage, sn = ((kt + 1) & 3) * kWStage;
+        const int qa = pa + so, qan = pa + sn;
+        const int qb[2] = {pb[0] + so, pb[1] + so}, qbn[2] = {pb[0] + sn, pb[1] + sn};
+        // substep 0; each fragment of substep 1 is read as soon as its last
+        // use here has issued
+        mfma_row(0);
+        read_a(qa, 1, 0);
+        mfma_row(1);
+        read_a(qa, 1, 1);
+        mfma_row(2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) read_b(qb, 1, j);
+        read_a(qa, 1, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-tile kt+3 into the stage k-tile kt-1 has left (every wave passed
+        // the barrier of the previous iteration after its reads of it)
+        if (kt > 0 && kt + 3 < nk) issue(T, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+        // substep 1
+        mfma_row(0);
+        mfma_row(1);
+        mfma_row(2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) {
+          // publish k-tile kt+1: k-tiles kt+2 and kt+3 may stay in flight
+          // (loads complete in issue order); a carried tile's first pass has
+          // landed already
+          const int after = min(2, nk - 2 - kt);
+          if (carried && kt + 1 < 4) {
+          } else if (after >= 2) wait_vm<2 * kWL>();
+          else if (after == 1) wait_vm<kWL>();
+          else wait_vm<0>();
+          barrier_lds();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) read_b(qbn, 0, j);
+#pragma unroll
+          for (int i = 0; i < 3; ++i) read_a(qan, 0, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vm<0>();
+    __syncthreads();
+    // every wave is done with the stage arrays: the next tile's first pass
+    have_nxt = w + per < wend;
+    if (have_nxt) {
+      nxt = setup(w + per);
+      if (nxt.nk > 0) issue_first(nxt);
+    }
+
+    // fp32 gradient rows straight from the accumulators: each store writes
+    // two whole 128-byte row pieces (lanes 0-31 and 32-63, four rows apart),
+    // through a buffer resource over this tile's rows (the entry point keeps
+    // them under 2 GiB), non-temporal (written once).  Row block wm + 4i,
+    // column block wn + 2j.
+    const int m0 = T.tm * WBM, n0 = T.tn * BN;
+    float* out = T.j < g.E ? g.grad_home + int64_t(T.j) * H * Hp
+                           : g.grad_pref + (int64_t(T.r) * g.B + (T.j - g.E)) * H * Hp;
+    const int trows = min(WBM, H - m0);
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        out + int64_t(m0) * Hp, 0, int(uint32_t(trows) * Hp * 4), 0x00020000);
+    int hb0 = wm * 32 + 4 * (lane >> 5);
+    const int nb0 = n0 + wn * 32 + (lane & 31);
+    asm volatile("" : "+v"(hb0));     // store offsets: computed here, not hoisted
+    auto store_tile = [&](auto full_) {
+      constexpr bool FULL = decltype(full_)::value;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = nb0 + 64 * j;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int h = hb0 + 128 * i + 8 * (v >> 2) + (v & 3);
+            if (FULL || (h < trows && n < Hp))
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), orsrc,
+                                                    int((uint32_t(h) * Hp + n) * 4), 0, kStoreNT);
+          }
+        }
+    };
+    if (m0 + WBM <= H && n0 + BN <= Hp) {
+      store_tile(std::true_type());
+    } else {
+      store_tile(std::false_type());
+      if (have_nxt) wait_vm<0>();      // see the carried wait above
     }
   }
 }
@@ -1263,7 +1640,10 @@ static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hi
     hipLaunchKernelGGL(k_sched<MODE_WGRAD>, dim3(1), dim3(1024), 0, stream, s);
     g.items = s.items;
     g.nitems = s.hdr;
-    hipLaunchKernelGGL((k_gemm<MODE_WGRAD, 4>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+    if (MOONEP_WGRAD_WIDE)
+      hipLaunchKernelGGL(k_wgrad, dim3(G), dim3(kWThreads), 0, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm<MODE_WGRAD, 4>), dim3(G), dim3(kGemmThreads), 0, stream, g);
     return hip_status();
   }
   const int kdepth = mode == MODE_DGRAD ? c->Hp : c->H;
@@ -1421,8 +1801,8 @@ extern "C" int moe_grouped_gemm_wgrad(const moe_cfg* cfg, const moe_plan* plan,
   const int rc = check_cfg(cfg);
   if (rc != MOE_OK) return rc;
   if (cfg->mode != MOE_MODE_TRAIN) return MOE_EINVAL;
-  // a 256-row fp32 gradient tile is stored through one 2 GiB buffer window
-  if (uint64_t(BM) * cfg->Hp * 4 >= (uint64_t(1) << 31)) return MOE_ELIMIT;
+  // a 384-row fp32 gradient tile is stored through one 2 GiB buffer window
+  if (uint64_t(WBM) * cfg->Hp * 4 >= (uint64_t(1) << 31)) return MOE_ELIMIT;
   if (!plan || !plan->cu_seqlens || !xperm || !dy || !grad_home || !workspace) return MOE_EINVAL;
   if (cfg->B > 0 && !grad_pref) return MOE_EINVAL;
   if (!aligned16(xperm, dy, grad_home, grad_pref, workspace)) return MOE_EINVAL;

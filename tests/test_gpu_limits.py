@@ -103,16 +103,17 @@ def test_gemms_at_the_offset_limit():
         rows_close(got, want)
 
 
-def test_wgrad_rejects_gradient_tiles_beyond_2gib():
-    """The weight gradient stores a 256-row fp32 tile through one buffer
-    window of 2 GiB, so H' must stay below 2^21; at 2^21 the host check
-    returns MOE_ELIMIT before any launch."""
-    c = mx.make_cfg(1, 4, 2, 1, 8, 1 << 21, 2, mx.MODE_TRAIN)
+@pytest.mark.parametrize("hp", [1398104, 1 << 21])
+def test_wgrad_rejects_gradient_tiles_beyond_2gib(hp):
+    """The weight gradient stores a 384-row fp32 tile through one buffer
+    window of 2 GiB, so 384 H' 4 bytes must stay below 2^31 (H' <= 1398101);
+    beyond, the host check returns MOE_ELIMIT before any launch."""
+    c = mx.make_cfg(1, 4, 2, 1, 8, hp, 2, mx.MODE_TRAIN)
     plan = mx.Plan(c)
     xperm = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")
-    dy = torch.zeros((4, 1 << 21), dtype=torch.bfloat16, device="cuda")
-    gh = torch.empty((2, 8, 1 << 21), dtype=torch.float32, device="cuda")
-    gp = torch.empty((2, 8, 1 << 21), dtype=torch.float32, device="cuda")
+    dy = torch.zeros((4, hp), dtype=torch.bfloat16, device="cuda")
+    gh = torch.empty((2, 8, hp), dtype=torch.float32, device="cuda")
+    gp = torch.empty((2, 8, hp), dtype=torch.float32, device="cuda")
     ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device="cuda")
     with pytest.raises(mx.MoeError) as ei:
         mx.moe_grouped_gemm_wgrad(c, plan, xperm, dy, gh, gp, ws)
