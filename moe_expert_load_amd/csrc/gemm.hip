@@ -899,10 +899,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     __syncthreads();
     // every wave is done with the stage arrays: start the next tile's loads
     if constexpr (kCarry) {
-      const int64_t wn = work_index(q + 1);
-      have_nxt = wn < wend;
+      const int64_t wnext = work_index(q + 1);
+      have_nxt = wnext < wend;
       if (have_nxt) {
-        nxt = setup(wn);
+        nxt = setup(wnext);
         if (nxt.nk > 0) issue_first(nxt);
       }
     }
