@@ -27,6 +27,8 @@ FLAGS = [
     # no packed fp32 arithmetic in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # a name declared again in an inner scope is an error, not a silent rebinding
+    "-Werror=shadow",
 ]
 
 

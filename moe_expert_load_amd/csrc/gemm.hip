@@ -1506,10 +1506,10 @@ __global__ __launch_bounds__(1024) void k_sched(SchedArgs s) {
       const int cost = a4 ? ((len + kBK - 1) / kBK + kNST - 1) / kNST * kNST + 12 : 0;
       __syncthreads();
       const int pc = block_scan(cost);
-      const int tc = s_part[16];
+      const int tsum = s_part[16];
       if (a4 && b4 < kMaxWItems) { s_wpre[b4] = s_wcarry + pc; s_wcost[b4] = cost; }
       __syncthreads();
-      if (tid == 0) s_wcarry += tc;
+      if (tid == 0) s_wcarry += tsum;
     }
     write_items(s.items, s.cap, b4, r, j, lo, len, 0, a4);
     if (a2) write_items(s.items2, s.cap_s, b2, r, j, lo, len, c4, 1);
