@@ -1239,7 +1239,11 @@ __global__ __launch_bounds__(kWThreads, 1) void k_wgrad(GemmArgs g) {
         const int qa = pa + so, qan = pa + sn;
         const int qb[2] = {pb[0] + so, pb[1] + so}, qbn[2] = {pb[0] + sn, pb[1] + sn};
         // substep 0; each fragment of substep 1 is read as soon as its last
-        // use here has issued
+        // use here has issued.  The wave runs this part at raised priority, so
+        // of a SIMD's two waves the one in substep 0 issues first and the
+        // pair settles into alternating phases (one multiplying while the
+        // other waits on its loads or the barrier)
+        __builtin_amdgcn_s_setprio(1);
         mfma_row(0);
         read_a(qa, 1, 0);
         mfma_row(1);
@@ -1248,6 +1252,7 @@ __global__ __launch_bounds__(kWThreads, 1) void k_wgrad(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) read_b(qb, 1, j);
         read_a(qa, 1, 2);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         // k-tile kt+3 into the stage k-tile kt-1 has left (every wave passed
         // the barrier of the previous iteration after its reads of it)
