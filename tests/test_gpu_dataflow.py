@@ -35,6 +35,9 @@ def shapes():
     yield W.TINY.with_(B=0, mode=1), "uniform", 2
     yield W.TINY.with_(H=72, Hp=40, S=37), "uniform", 3          # ragged H, Hp
     yield W.TINY.with_(R=2, E=4, S=300, K=2, B=2, H=192, Hp=264), "hot", 0   # long segments
+    # rows of more than 1,024 16-byte vectors; more routes per token than one batch (K = 12)
+    yield W.TINY.with_(name="wide_rows", H=9160, Hp=40, S=20), "uniform", 4
+    yield W.TINY.with_(name="many_routes", R=2, E=16, K=12, S=24, B=8, H=264, Hp=72), "uniform", 5
     for t in W.MAXVIO_SWEEP["skewed"]:
         yield W.SKEWED, "zipf", t
     yield W.SKEWED.with_(name="skewed_adv"), "theorem2", 0
