@@ -76,7 +76,6 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_bench_shape.txt")
 KERNEL_SOURCES = {"k_gemm<0>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_wgrad": "moe_expert_load_amd/csrc/gemm.hip",
-                  "k_gemm<1>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<2>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_gemm<3>": "moe_expert_load_amd/csrc/gemm.hip",
                   "k_swiglu_bwd": "moe_expert_load_amd/csrc/swiglu.hip",

@@ -22,8 +22,8 @@
 //               once per band rather than once per column tile.
 //   k_wgrad     the weight gradient G = xperm_seg^T @ dy_seg (fp32) on
 //               384 x 256 tiles with 8 waves (see its own comment).
-//   MODE 0: y = xperm_seg @ W (forward); MODE 1: the weight gradient on
-//   256 x 256 tiles (built with MOONEP_WGRAD_WIDE=0); MODE 2: dxperm_seg = dy_seg @ W^T (data
+//   MODE 0: y = xperm_seg @ W (forward); MODE 1: the weight gradient
+//   (k_wgrad only); MODE 2: dxperm_seg = dy_seg @ W^T (data
 //   gradient, over the forward's work list); MODE 3: the first projection
 //   of a SwiGLU expert, act = silu(x W_gate) * (x W_up) with W13 = [W_gate |
 //   W_up] in one [E+B, H, 2H'] tensor -- each 256-column tile takes 128
@@ -70,24 +70,6 @@ constexpr int BM = 256, BN = 256;
 #define MOONEP_FWD_NMAJOR 1
 #endif
 constexpr int kGemmThreads = 256;
-
-// Weight gradient: each XCD owns a contiguous range of items (segments),
-// balanced by predicted time, so all tiles of an item run on one XCD and
-// share its x^T and dy panels in that XCD's L2.
-#ifndef MOONEP_WGRAD_XCD
-#define MOONEP_WGRAD_XCD 1
-#endif
-
-// Weight gradient: the next tile's first k-tiles are loaded during the
-// current tile's store burst (1), or after it (0).
-#ifndef MOONEP_WGRAD_CARRY
-#define MOONEP_WGRAD_CARRY 1
-#endif
-
-// Weight gradient: 384 x 256 tiles (k_wgrad, 1) or 256 x 256 (k_gemm, 0).
-#ifndef MOONEP_WGRAD_WIDE
-#define MOONEP_WGRAD_WIDE 1
-#endif
 
 // Row-tile A operands interleave the two wave rows by 32-row blocks: wave
 // row wm holds tile rows 64 i + 32 wm + [0, 32), i = 0..3, so a tile with
@@ -304,7 +286,7 @@ struct GemmTile {
 // list, so each kernel holds one instance of the k-loop.
 template <int MODE, int NBK>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
-  static_assert(NBK == 4 || (MODE != MODE_WGRAD && (NBK == 2 || NBK == 1)), "tile class");
+  static_assert(MODE != MODE_WGRAD && (NBK == 4 || NBK == 2 || NBK == 1), "mode, tile class");
   using T = GemmTile<MODE>;
   constexpr int BK = T::BK, ROWB = T::ROWB, CPR = T::CPR, RSH = T::RSH, NI = T::NI;
   static_assert(NI * 4096 == kTile && (CPR == 4 || CPR == 8), "tile geometry");
@@ -313,9 +295,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wv >> 1, wn = wv & 1;
-  // Operand tiles: a "row tile" holds k-contiguous rows (forward A, and
-  // both operands of the data gradient), a "col tile" k-strided rows.
-  constexpr bool kRowA = MODE != MODE_WGRAD, kRowB = MODE == MODE_DGRAD;
+  // Operand tiles: A is always a "row tile" of k-contiguous rows; B is one
+  // too in the data gradient and a "col tile" (k-strided rows) otherwise.
+  constexpr bool kRowB = MODE == MODE_DGRAD;
   // Paired A tiles wherever A is a row tile (forward, data gradient, SwiGLU
   // projection).
   constexpr bool kPair = (MODE == MODE_FWD || MODE == MODE_DGRAD || MODE == MODE_SWIGLU) &&
@@ -325,17 +307,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       MODE == MODE_DGRAD || ((MODE == MODE_FWD || kSwi) && MOONEP_FWD_NMAJOR);
   const int H = g.H, Hp = g.Hp;
   const int WC = kSwi ? 2 * Hp : Hp;                     // weight / dy row length
-  const int ntm = MODE == MODE_WGRAD ? (H + BM - 1) / BM : 1;
   const int NOUT = MODE == MODE_DGRAD ? H : Hp;          // output columns
   // a SwiGLU tile yields 128 activation columns
   const int ntn = kSwi ? (Hp + BN / 2 - 1) / (BN / 2) : (NOUT + BN - 1) / BN;
-  const int64_t total = int64_t(*g.nitems) * ntm * ntn;
+  const int64_t total = int64_t(*g.nitems) * ntn;
   const int G = gridDim.x, per = G / 8;
   const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-  // XCD-owned item ranges (weight gradient): tiles [wbeg, wend) of this XCD
-  constexpr bool kXcdItems = MODE == MODE_WGRAD && MOONEP_WGRAD_XCD;
-  const int64_t wbeg = kXcdItems ? int64_t(g.nitems[8 + xcd]) * ntm * ntn : 0;
-  const int64_t wend = kXcdItems ? int64_t(g.nitems[9 + xcd]) * ntm * ntn : total;
 
   // Per-lane pieces of the transposing reads (col tiles), see lds_tr:
   // G4 = lane/16 picks the k half (G4/2) and the column half (G4%2).
@@ -391,19 +368,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   f32x16 acc[4][4];
   // Work index of this workgroup's q-th tile.
   auto work_index = [&](int64_t q) -> int64_t {
-    return kXcdItems ? wbeg + q * per + local : q * G + int64_t(xcd) * per + local;
+    return q * G + int64_t(xcd) * per + local;
   };
   const int arow = MODE == MODE_DGRAD ? Hp : H;          // A row length
   // Everything a tile's loads need: its place, its k-tile count, the two
   // range-checked operand resources and this lane's offsets into them.
   struct Tile {
     WorkItem it;
-    int tm, tn, KD, nk;
+    int tn, KD, nk;
     u32x4 ra, rb;
     uint32_t goa[NI], gob[NI];
   };
   auto setup = [&](int64_t w) -> Tile {
-    int tm, tn;
+    int tn;
     WorkItem it;
     if (kNMajor) {
       // Column-tile major inside bands of kBand row tiles of a segment: the
@@ -418,46 +395,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       const int b = loc / (kBand * ntn);
       const int bc = min(kBand, h.cnt - b * kBand);
       const int l = loc - b * kBand * ntn;
-      tm = 0;
       tn = l / bc;
       it = item_at(h.first + b * kBand + l % bc);
     } else {
-      const int64_t item = w / (ntm * ntn);
-      const int rest = (int)(w % (ntm * ntn));
-      tm = rest / ntn;
-      tn = rest % ntn;
-      it = item_at(item);
+      tn = (int)(w % ntn);
+      it = item_at(w / ntn);
     }
-    const int n0 = tn * BN, m0 = tm * BM;
-    const int KD = (MODE == MODE_FWD || kSwi) ? H : MODE == MODE_DGRAD ? Hp : it.rows;
-    // k-tiles: the weight gradient's K is the segment's row count, so it
-    // runs exactly the k-tiles that hold rows (the last one ragged: its rows
-    // past the segment load zeros); the fixed-K modes round up to whole
-    // passes over the stages (tiles past the end load zeros; ragged forward
-    // K is zeroed below)
-    const int nk = MODE == MODE_WGRAD ? (KD + BK - 1) / BK
-                                      : ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
+    const int n0 = tn * BN;
+    const int KD = MODE == MODE_DGRAD ? Hp : H;
+    // k-tiles, rounded up to whole passes over the stages (tiles past the end
+    // load zeros; a ragged K is zeroed below)
+    const int nk = ((KD + BK - 1) / BK + kNST - 1) / kNST * kNST;
 
-    // Operand A: forward = xperm rows of the segment (row tile); weight
-    // gradient = the same rows read as x^T (col tile over h); data gradient
-    // = dy rows (row tile over h').
-    // Operand B: forward = weight W(r, j) [H][Hp] (col tile); weight
-    // gradient = dy rows (col tile); data gradient = W(r, j) read as W^T,
-    // i.e. rows h of W with k = h' contiguous (row tile).
+    // Operand A: forward = xperm rows of the segment; data gradient = dy
+    // rows (row tiles, k = h or h' contiguous).
+    // Operand B: forward = weight W(r, j) [H][Hp] (col tile); data gradient
+    // = W(r, j) read as W^T, i.e. rows h of W with k = h' contiguous (row
+    // tile).
     const uint16_t* Abase = (MODE == MODE_DGRAD ? g.dy : g.xperm) + int64_t(it.row0) * arow;
-    const uint16_t* Bbase;
-    uint32_t bbytes;
-    if (MODE != MODE_WGRAD) {
-      Bbase = it.j < g.E ? g.w_home + int64_t(it.j) * H * WC
-                         : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * WC;
-      bbytes = uint32_t(H) * WC * 2;
-    } else {
-      Bbase = g.dy + int64_t(it.row0) * Hp;
-      bbytes = uint32_t(it.rows) * Hp * 2;
-    }
+    const uint16_t* Bbase = it.j < g.E ? g.w_home + int64_t(it.j) * H * WC
+                                       : g.w_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * WC;
+    const uint32_t bbytes = uint32_t(H) * WC * 2;
     Tile X;
     X.it = it;
-    X.tm = tm;
     X.tn = tn;
     X.KD = KD;
     X.nk = nk;
@@ -474,8 +434,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // col tile: load t covers k rows 2t, 2t+1 of 256 columns
       const int crow = t * 2 + (lane >> 5);
       const int cc = (lane & 31) ^ (4 * (crow & 3));
-      if (kRowA) X.goa[u] = uint32_t(rrow) * arow * 2 + rkc * 16;
-      else X.goa[u] = uint32_t(crow) * H * 2 + uint32_t(m0 + 8 * cc) * 2;
+      X.goa[u] = uint32_t(rrow) * arow * 2 + rkc * 16;
       // SwiGLU: 32-column block b of the tile is gate (b even) or up (b odd)
       // of activation columns tn*128 + (b/2)*32 + [0, 32).  Columns past the
       // activation width only feed accumulators that are never stored.
@@ -491,7 +450,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     constexpr int S = decltype(S_)::value;
     unsigned char* As = stage_a<S>();
     unsigned char* Bs = stage_b<S>();
-    const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+    const uint32_t ka = uint32_t(kt) * BK * 2;
     const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
@@ -510,20 +469,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     if constexpr (kNST == 5)
       if (X.nk > 4) issue_tile(X, std::integral_constant<int, 4 % kNST>(), 4);
   };
-  // Weight gradient: before a tile's stores go out, the next tile's first
-  // stages are issued, so its loads run during the store burst instead of
-  // after it (the stage arrays are free once the k-loop has ended).
-  constexpr bool kCarry = MODE == MODE_WGRAD && MOONEP_WGRAD_CARRY;
-  Tile nxt;
-  bool have_nxt = false;
   for (int64_t q = 0;; ++q) {
     const int64_t w = work_index(q);
-    if (w >= wend) break;
-    const bool carried = kCarry && have_nxt;
-    const Tile T = carried ? nxt : setup(w);
+    if (w >= total) break;
+    const Tile T = setup(w);
     const WorkItem it = T.it;
-    const int tm = T.tm, tn = T.tn, KD = T.KD, nk = T.nk;
-    const int n0 = tn * BN, m0 = tm * BM;
+    const int tn = T.tn, KD = T.KD, nk = T.nk;
+    const int n0 = tn * BN;
     const u32x4 ra = T.ra, rb = T.rb;
     uint32_t goa[NI], gob[NI];
 #pragma unroll
@@ -552,25 +504,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     // 64 NB rows): blocks past them are neither read nor multiplied.
     auto pipeline = [&](auto NB_) {
       constexpr int NB = decltype(NB_)::value;
-      // Direct loads of k-tile kt into stage S (= kt % kNST).
-      auto issue = [&](auto S_, int kt) {
-        constexpr int S = decltype(S_)::value;
-        unsigned char* As = stage_a<S>();
-        unsigned char* Bs = stage_b<S>();
-        const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
-        const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
-  #pragma unroll
-        for (int u = 0; u < NI; ++u) {
-          load_lds16(ra, As + (wv * NI + u) * 1024, goa[u], ka);
-          load_lds16(rb, Bs + (wv * NI + u) * 1024, gob[u], kb);
-        }
-      };
-      // Half h of those loads (A and B pieces u in [h*NI/2, (h+1)*NI/2)).
+      // Half h of the direct loads of k-tile kt into stage S (= kt % kNST):
+      // A and B pieces u in [h*NI/2, (h+1)*NI/2).
       auto issue_part = [&](auto S_, int kt, int h) {
         constexpr int S = decltype(S_)::value;
         unsigned char* As = stage_a<S>();
         unsigned char* Bs = stage_b<S>();
-        const uint32_t ka = kRowA ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * H * 2;
+        const uint32_t ka = uint32_t(kt) * BK * 2;
         const uint32_t kb = kRowB ? uint32_t(kt) * BK * 2 : uint32_t(kt) * BK * WC * 2;
   #pragma unroll
         for (int u2 = 0; u2 < NI / 2; ++u2) {
@@ -631,12 +571,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
   #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i >= NB) {
-          } else if (kRowA) {
+          } else {
             af[i] = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4*>(As + ra_off[s] + i * kABlock * ROWB));
-          } else {
-            const unsigned char* p = As + tr_off[i] + wm * 256 + s * 16 * 512;
-            af[i] = join(lds_tr(p), lds_tr(p + 4 * 512));
           }
         }
   #pragma unroll
@@ -673,7 +610,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // while the reads are in flight.
       auto interleave = [&]() {
         constexpr int NM = 4 * NB;                                    // MFMAs per substep
-        constexpr int NR = NB == 0 ? 0 : (kRowA ? NB : 8) + (kRowB ? 4 : 8);  // LDS reads
+        constexpr int NR = NB == 0 ? 0 : NB + (kRowB ? 4 : 8);    // LDS reads
         constexpr int X = NM < NR ? NM : NR;
   #pragma unroll
         for (int x = 0; x < X; ++x) {
@@ -688,9 +625,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       // At publish(kt) the loads of k-tiles kt+1 .. kt+kNST-2 may stay in flight.
       auto publish = [&](int kt) {
         const int after = min(kNST - 2, nk - 1 - kt);
-        // a carried tile's first pass has landed already (see below)
-        if (carried && kt < kNST) {
-        } else if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
+        if (kNST >= 5 && after >= 3) wait_vm<6 * NI>();
         else if (kNST >= 4 && after >= 2) wait_vm<4 * NI>();
         else if (kNST >= 3 && after == 1) wait_vm<2 * NI>();
         else wait_vm<0>();
@@ -702,7 +637,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         constexpr int S = decltype(S_)::value;
         constexpr int SN = (S + 1) % kNST;
         unsigned char* As = stage_a<S>();
-        if (kRowA && (kt + 1) * BK > KD) {
+        if ((kt + 1) * BK > KD) {
           // ragged K: row-tile chunks past the row length hold the next row's
           // data -- zero them and re-read this substep's fragments
           unsigned char* Bs = stage_b<S>();
@@ -854,15 +789,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         }
       } else if (nk > 0) {
       // k-tile 0 has landed once the later k-tiles of the first pass (2 NI
-      // loads each) are all that is left in flight.  A carried tile's first
-      // pass went out before the previous tile's stores: a full tile's 256
-      // store instructions per wave follow it (more than the 63 a wave keeps
-      // in flight, and completions count in issue order), and after a
-      // partial tile's stores the wave waited for everything -- so at most
-      // 62 pending operations leave the whole first pass landed.
-      if (carried) {
-        wait_vm<62>();
-      } else {
+      // loads each) are all that is left in flight.
+      {
         issue_first(T);
         const int later = min(nk, kNST) - 1;
         if constexpr (kNST >= 5) {
@@ -875,8 +803,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
       }
       barrier_lds();
       read_frags(std::integral_constant<int, 0>(), 0, fa0, fb0);
-      // nk need not be a multiple of kNST (weight gradient): stop after its
-      // last k-tile
+      // whole passes over the stages (the early exits never fire: nk is a
+      // multiple of kNST)
       for (int kt = 0; kt < nk; kt += kNST) {
         step(std::integral_constant<int, 0>(), kt);
         if (kt + 1 >= nk) break;
@@ -897,15 +825,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
     pipeline(std::integral_constant<int, NBK>());
     wait_vm<0>();
     __syncthreads();
-    // every wave is done with the stage arrays: start the next tile's loads
-    if constexpr (kCarry) {
-      const int64_t wnext = work_index(q + 1);
-      have_nxt = wnext < wend;
-      if (have_nxt) {
-        nxt = setup(wnext);
-        if (nxt.nk > 0) issue_first(nxt);
-      }
-    }
 
     // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and
     // rows 8*(v/4) + 4*(l/32) + v%4 of its block for v = 0..15.
@@ -970,7 +889,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
       __syncthreads();
-    } else if (MODE != MODE_WGRAD) {
+    } else {
       // Per wave, two passes of 64 rows x 128 columns staged as bf16 in the
       // wave's own 16 KB stage array (256-byte rows; pairs of rows converted
       // by one hardware instruction), then whole 16-byte row chunks to global
@@ -1016,46 +935,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-      __syncthreads();
-    } else {
-      // fp32 gradient rows straight from the accumulators: each store
-      // instruction writes two whole 128-byte row pieces (lanes 0-31 and
-      // 32-63, four rows apart).  Full tiles skip the bounds checks.  Buffer
-      // stores (non-temporal) over this tile's rows: 32-bit offsets from one
-      // descriptor instead of a 64-bit address per store (1.3 % faster); the
-      // entry point keeps a tile's rows under 2 GiB (384 H' 4 < 2^31).
-      float* out = it.j < g.E ? g.grad_home + int64_t(it.j) * H * Hp
-                              : g.grad_pref + (int64_t(it.r) * g.B + (it.j - g.E)) * H * Hp;
-      const int trows = min(BM, H - m0);
-      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-          out + int64_t(m0) * Hp, 0, int(uint32_t(trows) * Hp * 4), 0x00020000);
-      const int hb0 = wm * 128 + 4 * (lane >> 5);              // row in the tile
-      const int nb0 = n0 + wn * 128 + (lane & 31);
-      auto store_tile = [&](auto full_) {
-        constexpr bool FULL = decltype(full_)::value;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = nb0 + 32 * j;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int h = hb0 + 32 * i + 8 * (v >> 2) + (v & 3);
-              if (FULL || (h < trows && n < Hp))   // written once: streaming store
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), orsrc,
-                                                      int((uint32_t(h) * Hp + n) * 4), 0,
-                                                      kStoreNT);
-            }
-          }
-      };
-      if (m0 + BM <= H && n0 + BN <= Hp) {
-        store_tile(std::true_type());
-      } else {
-        store_tile(std::false_type());
-        // a partial tile's stores may be fewer than the carried loads' wait
-        // assumes (see the pipeline): wait for everything
-        if (kCarry && have_nxt) wait_vm<0>();
       }
       __syncthreads();
     }
@@ -1645,10 +1524,7 @@ static int launch_gemm(int mode, const moe_cfg* c, GemmArgs& g, SchedArgs& s, hi
     hipLaunchKernelGGL(k_sched<MODE_WGRAD>, dim3(1), dim3(1024), 0, stream, s);
     g.items = s.items;
     g.nitems = s.hdr;
-    if (MOONEP_WGRAD_WIDE)
-      hipLaunchKernelGGL(k_wgrad, dim3(G), dim3(kWThreads), 0, stream, g);
-    else
-      hipLaunchKernelGGL((k_gemm<MODE_WGRAD, 4>), dim3(G), dim3(kGemmThreads), 0, stream, g);
+    hipLaunchKernelGGL(k_wgrad, dim3(G), dim3(kWThreads), 0, stream, g);
     return hip_status();
   }
   const int kdepth = mode == MODE_DGRAD ? c->Hp : c->H;

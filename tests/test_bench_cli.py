@@ -20,14 +20,14 @@ def test_stats_summary_from_a_small_csv(tmp_path):
     csv = tmp_path / "k_stats.csv"
     csv.write_text(
         '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
-        '"void moonep::k_gemm<1>(moonep::GemmArgs)",2,34000000,17000000,60.0,16900000,17100000,1\n'
+        '"void moonep::k_gemm<2>(moonep::GemmArgs)",2,34000000,17000000,60.0,16900000,17100000,1\n'
         '"void moonep::k_dispatch<4>(int)",2,3200000,1600000,40.0,1590000,1610000,1\n')
     out = tmp_path / "summary.md"
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-stats",
                         str(csv), "cmd", str(out)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     text = out.read_text()
-    assert "| k_gemm<1> | 2 | 17000.0 |" in text
+    assert "| k_gemm<2> | 2 | 17000.0 |" in text
     assert "| k_dispatch | 2 | 1600.0 |" in text
 
 
