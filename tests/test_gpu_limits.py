@@ -118,3 +118,41 @@ def test_wgrad_rejects_gradient_tiles_beyond_2gib(hp):
     with pytest.raises(mx.MoeError) as ei:
         mx.moe_grouped_gemm_wgrad(c, plan, xperm, dy, gh, gp, ws)
     assert ei.value.code == mx.MOE_ELIMIT
+
+
+def test_wgrad_at_the_2gib_tile_window():
+    """The largest H' the weight gradient takes (1,398,096, a multiple of 8
+    at or below 1,398,101): a full 384-row tile then spans 384 H' 4 =
+    2,147,475,456 bytes of its store window, 8 KB short of 2^31, and H = 400
+    leaves a second, 16-row tile.  Sampled gradient rows (both tiles, their
+    first and last rows) of both experts against the oracle's sampled form,
+    within 2e-2 per row."""
+    hp = 1398096
+    assert 384 * hp * 4 < 2 ** 31 <= 384 * (hp + 8) * 4
+    s = W.TINY.with_(name="wgrad_window", R=1, S=32, E=2, K=1, H=400, Hp=hp, B=2, cfg_id=8)
+    c, oc = cfgs(s)
+    ids, _ = W.routing_uniform(s)
+    ref = make_plan(ids, oc)
+    plan, g = gpu_plan(s, ids)
+    assert_plan_equal(g, ref, s)
+    announce("weight gradient at the 2 GiB tile window", s)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    rows = s.R * s.SK
+    x = W.randn_bf16((s.tokens, s.H), 81, "cuda")
+    dy = W.randn_bf16((rows, s.Hp), 82, "cuda")
+    xp = torch.empty((rows, s.H), **bf)
+    gh = torch.full((s.E, s.H, s.Hp), 3.0, dtype=torch.float32, device="cuda")
+    gp = torch.full((s.R * s.B, s.H, s.Hp), 3.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mx.moe_gemm_workspace_size(c), dtype=torch.uint8, device="cuda")
+    mx.moe_dispatch(c, plan, x, xp)
+    mx.moe_grouped_gemm_wgrad(c, plan, xp, dy, gh, gp, ws)
+    torch.cuda.synchronize()
+    hs = np.array([0, 1, 200, 382, 383, 384, 390, 399], np.int64)
+    hcols = torch.as_tensor(hs, device="cuda")
+    xcols = DeviceRows(x.index_select(1, hcols).contiguous())
+    for j in range(s.E):                       # R = 1: both experts are home rows
+        want = dataflow.wgrad_entries(0, j, np.arange(hs.size), xcols, DeviceRows(dy), ref, oc)
+        got = gh[j].index_select(0, hcols).cpu().numpy()
+        rows_close(got, want)
+    # one rank: no prefetch slot, so the prefetch gradients stay as they were
+    assert bool((gp[:, ::97, ::4099] == 3.0).all())
