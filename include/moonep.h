@@ -116,8 +116,10 @@ enum {
 };
 
 /* Limits checked on the host (MOE_ELIMIT beyond them).  Besides these:
- * R*S*K < 2^31 slots, one weight matrix H*Hp*2 bytes < 4 GiB and one rank's
- * permuted rows S*K*max(H, Hp)*2 bytes < 4 GiB. */
+ * R*S*K < 2^31 slots, R*S < 2^24 tokens (dispatch runs one 256-thread
+ * workgroup per token, and one launch holds fewer than 2^32 threads), one
+ * weight matrix H*Hp*2 bytes < 4 GiB and one rank's permuted rows
+ * S*K*max(H, Hp)*2 bytes < 4 GiB. */
 #define MOE_MAX_E 2048
 #define MOE_MAX_R 1024
 #define MOE_MAX_K 64

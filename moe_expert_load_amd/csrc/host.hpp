@@ -24,6 +24,9 @@ inline int check_cfg(const moe_cfg* c) {
   if (c->B > n) return MOE_EINVAL;
   if (c->E > MOE_MAX_E || c->R > MOE_MAX_R || c->K > MOE_MAX_K) return MOE_ELIMIT;
   if (i64(c->R) * i64(c->S) * i64(c->K) >= (int64_t(1) << 31)) return MOE_ELIMIT;
+  // dispatch and its backward run one 256-thread workgroup per token, and one
+  // launch holds fewer than 2^32 threads
+  if (i64(c->R) * i64(c->S) >= (int64_t(1) << 24)) return MOE_ELIMIT;
   // byte extents the GEMM's 32-bit buffer offsets cover: one weight matrix,
   // and one rank's permuted rows
   const int64_t wide = c->H > c->Hp ? c->H : c->Hp;

@@ -77,6 +77,11 @@ def test_host_only_calls_and_validation():
     with pytest.raises(mx.MoeError) as ei:
         mx.moe_plan_sizes(mx.make_cfg(64, 1 << 20, 896, 64, 128, 64, 14))
     assert ei.value.code == mx.MOE_ELIMIT
+    # tokens: R*S < 2^24 (one 256-thread workgroup per token in dispatch)
+    mx.moe_plan_sizes(mx.make_cfg(1024, (1 << 14) - 1, 1024, 1, 8, 8, 1))
+    with pytest.raises(mx.MoeError) as ei:
+        mx.moe_plan_sizes(mx.make_cfg(1024, 1 << 14, 1024, 1, 8, 8, 1))
+    assert ei.value.code == mx.MOE_ELIMIT
     # inference may use fewer slots, even none
     mx.moe_plan_sizes(mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 4, mx.MODE_INFER))
     mx.moe_plan_sizes(mx.make_cfg(8, 8192, 384, 8, 7168, 2048, 0, mx.MODE_INFER))
