@@ -948,8 +948,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmArgs g) {
 // by the matrix pipe, so what counts is operand bytes per multiply-add: a
 // 384 x 256 tile needs (384 + 256) / (384 * 256) of them per k, a sixth less
 // than a 256 x 256 tile.  Its 384 KB of fp32 accumulators take 8 waves (2 per
-// SIMD), each with 3 x 4 MFMA blocks of 32 x 32 (192 AGPRs) and at most 64
-// other registers, so the layout is chosen to need few per-lane offsets:
+// SIMD), each with 3 x 4 MFMA blocks of 32 x 32 (192 accumulator registers,
+// which the compiler keeps in ordinary VGPRs: two waves per SIMD leave each
+// 256 registers in all) and at most 64 other registers, so the layout is
+// chosen to need few per-lane offsets:
 //  * wave (wm, wn) = (wave % 4, wave / 4) takes the tile's 32-row blocks
 //    wm + 4i (i < 3) and 32-column blocks wn + 2j (j < 4);
 //  * a stage holds x^T as three [32 k][128 h] sub-tiles (256-byte rows) and
