@@ -130,7 +130,10 @@ __device__ __forceinline__ void load_lds16(u32x4 rsrc, const unsigned char* lds_
 #pragma unroll
   for (int q = 0; q < 4; ++q) r[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc[q]);
   const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  // one wait state between the scalar write of M0 and the LDS-DMA load that
+  // reads it (a hazard of this GPU generation that the compiler's hazard pass
+  // cannot see inside inline assembly)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(l), "v"(voff), "s"(r), "s"(so) : "memory");
 }
 
