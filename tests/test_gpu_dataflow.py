@@ -41,11 +41,18 @@ def shapes():
     for t in W.MAXVIO_SWEEP["skewed"]:
         yield W.SKEWED, "zipf", t
     yield W.SKEWED.with_(name="skewed_adv"), "theorem2", 0
+    # an expert named twice in one token's row: every slot is routed on its own
+    yield W.TINY.with_(name="repeated_ids", K=3), "repeat", 6
 
 
 def routing(shape, kind, arg):
     if kind == "uniform":
         return W.routing_uniform(shape, salt=arg)
+    if kind == "repeat":
+        ids, gates = W.routing_uniform(shape, salt=arg)
+        ids = ids.copy()
+        ids[::3, 1] = ids[::3, 0]                   # every third token repeats its first expert
+        return ids, gates
     if kind == "zipf":
         ids, gates, _, _ = W.routing_zipf(shape, arg)
         return ids, gates

@@ -27,7 +27,8 @@ def _gpu():
 
 CASES = [(W.TINY, "uniform"), (W.TINY, "hot"), (W.TINY.with_(B=1, mode=1), "uniform"),
          (W.TINY.with_(R=2, E=8, K=3, S=10, B=4), "uniform"), (W.SKEWED, "zipf"),
-         (W.SKEWED.with_(name="skewed_adv"), "theorem2")]
+         (W.SKEWED.with_(name="skewed_adv"), "theorem2"),
+         (W.TINY.with_(name="repeated_ids", K=3), "repeat")]
 
 
 def ids_of(shape, kind):
@@ -37,6 +38,10 @@ def ids_of(shape, kind):
         return W.routing_theorem2(shape)
     if kind == "zipf":
         return W.routing_zipf(shape, 10.0)[0]
+    if kind == "repeat":                            # an expert named twice in a row
+        ids = W.routing_uniform(shape, salt=2)[0].copy()
+        ids[::3, 1] = ids[::3, 0]
+        return ids
     return W.routing_uniform(shape, salt=2)[0]
 
 
